@@ -1,0 +1,201 @@
+/*
+ * gca.h -- C ABI of the Grouped Cross Attention (GCA) hot path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * GCA is the retrieval attention of the Differentiable Retrieval-based
+ * Transformer ("Efficient Length-Generalizable Attention via Causal Retrieval
+ * for Long-Context Language Modeling", Hu et al., ICML 2025).  The sequence is
+ * cut into chunks of S tokens; each query chunk uses a landmark vector to score
+ * past chunks, keeps the top-k, attends to each retrieved chunk separately and
+ * fuses the k results with softmax-normalised relevance weights.
+ *
+ * Three calls cover the path, in the order a training step makes them:
+ *   gca_retrieve  -- relevance scores, top-k selection, fusion weights
+ *   gca_forward   -- per-chunk attention of every token + weighted fusion
+ *   gca_backward  -- gradients of Q, K, V, the weights, the scores and the
+ *                    landmarks
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *   never allocates or frees device memory and keeps no state except a
+ *   thread-local error string.
+ * - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *   return without synchronising.
+ * - All arrays are dense, contiguous, row-major, with the layouts given below.
+ *   G (retrieval groups) is an independent leading axis: every (g, b, h) slice
+ *   is a separate problem.  Tensors named "big" below must be 16-byte aligned,
+ *   the others 4-byte aligned.
+ * - Outputs are fully overwritten.  Empty slots (fewer candidates than k, or an
+ *   index outside [0, n_key) passed to forward/backward) read as idx = -1,
+ *   score = w = dw = dscore = 0 and lse = -inf; chunks nobody retrieved get
+ *   dk = dv = dlk = 0.
+ * - Every argument is checked before anything is launched.  On failure the call
+ *   returns GCA_ERR_INVALID_ARGUMENT / GCA_ERR_UNSUPPORTED / GCA_ERR_WORKSPACE,
+ *   touches no output and sets gca_last_error().  A failed launch returns
+ *   GCA_ERR_DEVICE with the HIP error text in gca_last_error().
+ * - Setting the environment variable GCA_DEBUG_SYNC=1 makes every call
+ *   synchronise its stream and check for device errors before returning.
+ *
+ * Supported sizes (anything else returns GCA_ERR_UNSUPPORTED):
+ *   dtype GCA_BF16 : chunk_size 64, head_dim 64, landmark_dim 32 or 64
+ *   dtype GCA_F32  : chunk_size 1..64, head_dim 1..64, landmark_dim 1..128
+ *   top_k 1..16; gca_backward additionally needs n_query * top_k <= 16384.
+ */
+#ifndef GCA_H
+#define GCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GCA_ABI_VERSION 1
+
+typedef int gca_status;
+enum {
+  GCA_OK = 0,
+  GCA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or flag */
+  GCA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (see sizes above) */
+  GCA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+  GCA_ERR_DEVICE = 4            /* a HIP launch or device error */
+};
+
+typedef int gca_dtype;
+enum {
+  GCA_F32 = 0, /* float32 q, k, v, o, dout, dq, dk, dv, lq, lk */
+  GCA_BF16 = 1 /* bfloat16 for the same tensors; accumulation is float32 */
+};
+
+/* Problem description shared by the three calls. */
+typedef struct {
+  int64_t G;            /* retrieval groups (independent problems)          */
+  int64_t B;            /* batch                                            */
+  int64_t H;            /* heads; retrieval is per (g, b, h)                */
+  int64_t n_query;      /* Nq: query chunks                                 */
+  int64_t n_key;        /* Nk: resident (candidate) chunks                  */
+  int32_t chunk_size;   /* S: tokens per chunk (query and key chunks)       */
+  int32_t head_dim;     /* D                                                */
+  int32_t landmark_dim; /* Dl: length of one landmark vector per head       */
+  int32_t top_k;        /* k: chunks retrieved per query chunk              */
+  int32_t dtype;        /* gca_dtype of the "big" tensors                   */
+  int32_t softmax_one;  /* 0: softmax fusion weights; 1: softmax off-by-one */
+  float attn_scale;     /* token logit scale, usually 1/sqrt(D)             */
+  float score_scale;    /* relevance score scale, usually 1/sqrt(Dl)        */
+} gca_shape;
+
+/* Returns GCA_ABI_VERSION of the loaded library. */
+int gca_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* gca_status_string(gca_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* gca_last_error(void);
+
+/* Device workspace needed by an operation: op 0 = gca_retrieve,
+ * 1 = gca_forward (always 0), 2 = gca_backward.  *bytes receives the size;
+ * a workspace of at least that many bytes, 256-byte aligned, must be passed. */
+gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes);
+
+/*
+ * gca_retrieve -- Eq. 1 relevance scores, top-k and Eq. 3 fusion weights.
+ *
+ * Definition: paperhub.cn review page, authors' reply "Cmt 1" (score of past
+ * chunk j for query chunk t is <lq_t, lk_j> / sqrt(d)); long-context-modeling
+ * README, "Model Architecture" (a chunk retrieves the top-k past chunks with the
+ * landmark of the chunk before it; their softmax-normalised scores are the
+ * fusion weights); paperhub.cn, authors' reply "Q4" (softmax off-by-one).
+ *
+ * For every (g, b, h, t):  candidates j = 0 .. min(q_pos[t] - 1, n_key) - 1,
+ *   r_j = score_scale * <lq[g,b,h,t,:], lk[g,b,h,j,:]>   (float32 accumulate)
+ *   the min(k, #candidates) best by (r descending, j ascending) are written to
+ *   idx[.., 0:m] in ascending j, with score = r and
+ *   w = e^r / sum e^r               (softmax_one = 0)
+ *   w = e^r / (1 + sum e^r)         (softmax_one = 1), sums over the m kept.
+ *
+ *   lq    [G, B, H, Nq, Dl]   dtype, big        query landmarks
+ *   lk    [G, B, H, Nk, Dl]   dtype, big        candidate landmarks
+ *   q_pos [Nq]                int32             chunk position of each query
+ *                                               chunk (training: q_pos[t] = t)
+ *   idx   [G, B, H, Nq, k]    int32   output
+ *   score [G, B, H, Nq, k]    float32 output
+ *   w     [G, B, H, Nq, k]    float32 output
+ *   ws / ws_bytes             workspace (gca_workspace_size op 0)
+ */
+gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
+                        const int32_t* q_pos, int32_t* idx, float* score, float* w,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gca_forward -- Eq. 2 per-chunk attention and Eq. 3 weighted fusion.
+ *
+ * Definition: long-context-modeling README, "Model Architecture" (first stage:
+ * each token attends to the tokens of each retrieved chunk separately, giving
+ * O^i; second stage: weighted sum of the O^i); paperlayer.ai summary,
+ * appendix B (the kernel returns O and the log-sum-exp L).
+ *
+ * For every (g, b, h, t), token x < S and slot i with c = idx[.., t, i] in
+ * [0, n_key):
+ *   s_j   = attn_scale * <q[.., t, x, :], k[.., c, j, :]>,  j < S (no mask)
+ *   lse   = log sum_j exp(s_j)            -> lse[.., t, i, x]
+ *   O^i   = sum_j exp(s_j - lse) v[.., c, j, :]
+ *   o[.., t, x, :] = sum_i w[.., t, i] * O^i   (float32, rounded once)
+ *
+ *   q     [G, B, H, Nq, S, D]  dtype, big
+ *   k, v  [G, B, H, Nk, S, D]  dtype, big
+ *   idx   [G, B, H, Nq, k]     int32      (from gca_retrieve, any order)
+ *   w     [G, B, H, Nq, k]     float32
+ *   o     [G, B, H, Nq, S, D]  dtype, big, output
+ *   lse   [G, B, H, Nq, k, S]  float32 output, may be NULL (then not written;
+ *                              gca_backward needs it)
+ */
+gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
+                       const void* v, const int32_t* idx, const float* w, void* o,
+                       float* lse, void* stream);
+
+/*
+ * gca_backward -- gradients of the forward and of the fusion weights/scores.
+ *
+ * Definition: paperlayer.ai summary, appendix B (the backward returns gradients
+ * for Q, K, V and the weights); long-context-modeling README, "Model
+ * Architecture" (back-propagation reaches the retrieval scores through the
+ * weights); Eq. 1 as for gca_retrieve.  With dO = dL/do:
+ *   dw_i   = sum_x <dO[x], O^i[x]>
+ *   dS     = w_i P (dO v_c^T - rowsum(dO * O^i))        per (t, i) pair
+ *   dq_t  += attn_scale dS k_c,   dk_c += attn_scale dS^T q_t,
+ *   dv_c  += w_i P^T dO
+ *   dscore_i = w_i (dw_i - sum_l w_l dw_l)   (valid for both weight forms,
+ *                                            w must come from gca_retrieve)
+ *   dlq_t += score_scale sum_i dscore_i lk_c,   dlk_c += score_scale dscore_i lq_t
+ * Top-k selection is treated as fixed.  Sums over (t, i) run in a fixed order,
+ * so results are bitwise reproducible.
+ *
+ *   q, dout        [G, B, H, Nq, S, D]  dtype, big
+ *   k, v           [G, B, H, Nk, S, D]  dtype, big
+ *   idx, w         [G, B, H, Nq, k]     int32 / float32 (as passed to forward)
+ *   lse            [G, B, H, Nq, k, S]  float32 from gca_forward
+ *   lq, lk         landmarks as in gca_retrieve; may be NULL only if dlq/dlk
+ *                  (respectively dlk/dlq) are NULL
+ *   dq             [G, B, H, Nq, S, D]  dtype output
+ *   dk, dv         [G, B, H, Nk, S, D]  dtype output
+ *   dw, dscore     [G, B, H, Nq, k]     float32 output
+ *   dlq            [G, B, H, Nq, Dl]    float32 output or NULL
+ *   dlk            [G, B, H, Nk, Dl]    float32 output or NULL
+ *   ws / ws_bytes  workspace (gca_workspace_size op 2)
+ * dlq needs lk; dlk needs lq.
+ */
+gca_status gca_backward(const gca_shape* shape, const void* q, const void* k,
+                        const void* v, const int32_t* idx, const float* w,
+                        const float* lse, const void* dout, const void* lq,
+                        const void* lk, void* dq, void* dk, void* dv, float* dw,
+                        float* dscore, float* dlq, float* dlk, void* ws,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* GCA_H */

@@ -1,0 +1,165 @@
+"""Python binding of libgca.so, the MI355X (gfx950) Grouped Cross Attention library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Functions take torch tensors that live in device memory (PyTorch is
+used for device memory and streams) and enqueue work on torch's current
+stream.  The entry points mirror the C ABI in include/gca.h:
+
+  gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None)
+  gca_forward(shape, q, k, v, idx, w, o, lse=None)
+  gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
+               dlq=None, dlk=None, ws=None)
+  gca_workspace_size(shape, op)          op: 0 retrieve, 1 forward, 2 backward
+
+A missing library raises; there is no fallback path.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
+           "load", "gca_abi_version", "gca_status_string", "gca_last_error",
+           "gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "OP_RETRIEVE",
+           "OP_FORWARD", "OP_BACKWARD", "EXPORTED"]
+
+GCA_F32 = 0
+GCA_BF16 = 1
+OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
+EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
+            "gca_retrieve", "gca_forward", "gca_backward")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class GcaShape(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_int64), ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("n_query", ctypes.c_int64), ("n_key", ctypes.c_int64),
+                ("chunk_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("landmark_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_one", ctypes.c_int32),
+                ("attn_scale", ctypes.c_float), ("score_scale", ctypes.c_float)]
+
+
+class GcaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{gca_status_string(status)}: {message}")
+        self.status = status
+
+
+def make_shape(G, B, H, n_query, n_key, chunk_size, head_dim, landmark_dim, top_k, dtype,
+               softmax_one=0, attn_scale=None, score_scale=None):
+    return GcaShape(G, B, H, n_query, n_key, chunk_size, head_dim, landmark_dim, top_k, dtype,
+                    int(softmax_one),
+                    1.0 / math.sqrt(head_dim) if attn_scale is None else attn_scale,
+                    1.0 / math.sqrt(landmark_dim) if score_scale is None else score_scale)
+
+
+def library_path():
+    return os.environ.get("GCA_LIBRARY", os.path.join(_HERE, "libgca.so"))
+
+
+_lib = None
+
+
+def load():
+    """Loads libgca.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with retrieval_sparse_attention_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sp = ctypes.POINTER(GcaShape)
+    lib.gca_abi_version.restype = ctypes.c_int
+    lib.gca_abi_version.argtypes = []
+    lib.gca_status_string.restype = ctypes.c_char_p
+    lib.gca_status_string.argtypes = [ctypes.c_int]
+    lib.gca_last_error.restype = ctypes.c_char_p
+    lib.gca_last_error.argtypes = []
+    lib.gca_workspace_size.restype = ctypes.c_int
+    lib.gca_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.gca_retrieve.restype = ctypes.c_int
+    lib.gca_retrieve.argtypes = [sp] + [vp] * 6 + [vp, sz, vp]
+    lib.gca_forward.restype = ctypes.c_int
+    lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
+    lib.gca_backward.restype = ctypes.c_int
+    lib.gca_backward.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def gca_abi_version():
+    return load().gca_abi_version()
+
+
+def gca_status_string(status):
+    return load().gca_status_string(int(status)).decode()
+
+
+def gca_last_error():
+    return load().gca_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise GcaError(status, gca_last_error())
+
+
+def _ptr(t, name):
+    """Device address of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def gca_workspace_size(shape, op):
+    n = ctypes.c_size_t(0)
+    _check(load().gca_workspace_size(ctypes.byref(shape), int(op), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(shape, op, ws, like):
+    if ws is not None:
+        return ws
+    n = gca_workspace_size(shape, op)
+    if n == 0:
+        return None
+    import torch
+    return torch.empty(n, dtype=torch.uint8, device=like.device)
+
+
+def gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None):
+    ws = _workspace(shape, OP_RETRIEVE, ws, lq)
+    _check(load().gca_retrieve(
+        ctypes.byref(shape), _ptr(lq, "lq"), _ptr(lk, "lk"), _ptr(q_pos, "q_pos"),
+        _ptr(idx, "idx"), _ptr(score, "score"), _ptr(w, "w"), _ptr(ws, "ws"),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_forward(shape, q, k, v, idx, w, o, lse=None):
+    _check(load().gca_forward(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(idx, "idx"),
+        _ptr(w, "w"), _ptr(o, "o"), _ptr(lse, "lse"), _stream()))
+
+
+def gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
+                 dlq=None, dlk=None, ws=None):
+    ws = _workspace(shape, OP_BACKWARD, ws, q)
+    _check(load().gca_backward(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(idx, "idx"),
+        _ptr(w, "w"), _ptr(lse, "lse"), _ptr(dout, "dout"), _ptr(lq, "lq"), _ptr(lk, "lk"),
+        _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"), _ptr(dw, "dw"), _ptr(dscore, "dscore"),
+        _ptr(dlq, "dlq"), _ptr(dlk, "dlk"), _ptr(ws, "ws"),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))

@@ -1,0 +1,376 @@
+// C ABI of the GCA hot path: argument checks, workspace sizing and launches.
+// Everything here runs on the host; the checks finish before any HIP call, so
+// a rejected call has touched neither the device nor any output.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "gca.h"
+#include "gca_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gca_status fail(gca_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("GCA_DEBUG_SYNC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+gca_status device_status(hipError_t e, hipStream_t stream, const char* what) {
+  if (e == hipSuccess && debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess)
+    return fail(GCA_ERR_DEVICE, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  g_err[0] = '\0';
+  return GCA_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+enum Op { kRetrieve = 0, kForward = 1, kBackward = 2 };
+
+struct Sizes {
+  int64_t heads;    // G * B * H
+  int64_t q_rows;   // heads * n_query
+  int64_t k_rows;   // heads * n_key
+  int64_t q_elems;  // q_rows * S * D
+  int64_t k_elems;  // k_rows * S * D
+  int64_t slots;    // q_rows * top_k
+};
+
+gca_status check_shape(const gca_shape* s, int op, Sizes* z) {
+  if (s == nullptr) return fail(GCA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->G < 1 || s->B < 1 || s->H < 1)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "G, B, H must be >= 1 (got %lld, %lld, %lld)",
+                (long long)s->G, (long long)s->B, (long long)s->H);
+  if (s->n_query < 0 || s->n_key < 0)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "n_query and n_key must be >= 0");
+  if (s->n_key > 0x7ffffffeLL)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "n_key must be below 2^31 - 1");
+  if (s->chunk_size < 1 || s->head_dim < 1 || s->landmark_dim < 1)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "chunk_size, head_dim, landmark_dim must be >= 1");
+  if (s->top_k < 1) return fail(GCA_ERR_INVALID_ARGUMENT, "top_k must be >= 1");
+  if (s->top_k > 16) return fail(GCA_ERR_UNSUPPORTED, "top_k > 16 is not supported");
+  if (s->dtype != GCA_F32 && s->dtype != GCA_BF16)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "dtype must be GCA_F32 or GCA_BF16");
+  if (s->softmax_one != 0 && s->softmax_one != 1)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "softmax_one must be 0 or 1");
+  if (!std::isfinite(s->attn_scale) || !std::isfinite(s->score_scale))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "attn_scale and score_scale must be finite");
+  if (s->dtype == GCA_BF16) {
+    if (op != kRetrieve && (s->chunk_size != 64 || s->head_dim != 64))
+      return fail(GCA_ERR_UNSUPPORTED, "bf16 attention needs chunk_size = head_dim = 64");
+    if (op != kForward && s->landmark_dim != 32 && s->landmark_dim != 64)
+      return fail(GCA_ERR_UNSUPPORTED, "bf16 landmarks need landmark_dim 32 or 64");
+  } else {
+    if (s->chunk_size > 64 || s->head_dim > 64)
+      return fail(GCA_ERR_UNSUPPORTED, "f32 attention needs chunk_size, head_dim <= 64");
+    if (s->landmark_dim > 128)
+      return fail(GCA_ERR_UNSUPPORTED, "f32 landmarks need landmark_dim <= 128");
+  }
+  Sizes t{};
+  int64_t gb, td;
+  if (!mul_ok(s->G, s->B, &gb) || !mul_ok(gb, s->H, &t.heads) ||
+      !mul_ok(t.heads, s->n_query, &t.q_rows) || !mul_ok(t.heads, s->n_key, &t.k_rows) ||
+      !mul_ok((int64_t)s->chunk_size, s->head_dim, &td) || !mul_ok(t.q_rows, td, &t.q_elems) ||
+      !mul_ok(t.k_rows, td, &t.k_elems) || !mul_ok(t.q_rows, s->top_k, &t.slots) ||
+      t.q_elems > (int64_t(1) << 50) || t.k_elems > (int64_t(1) << 50))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "tensor sizes overflow");
+  if (t.q_rows > 0x7fffffffLL || t.k_rows > 0x7fffffffLL)
+    return fail(GCA_ERR_UNSUPPORTED, "more than 2^31 - 1 query or key chunk tiles");
+  if (op == kBackward && s->n_query * (int64_t)s->top_k > 0x7fffffffLL)
+    return fail(GCA_ERR_UNSUPPORTED, "n_query * top_k must be below 2^31");
+  if (z) *z = t;
+  return GCA_OK;
+}
+
+gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
+  gca::ScanPlan p{};
+  p.kmax = s->top_k <= 4 ? 4 : (s->top_k <= 8 ? 8 : 16);
+  p.n_qtiles = (int)((s->n_query + 31) / 32);
+  p.nsplit = 1;
+  p.split_len = 128;
+  if (s->dtype != GCA_BF16 || s->n_key <= 1024) {
+    p.split_len = ((s->n_key + 127) / 128) * 128;
+    if (p.split_len == 0) p.split_len = 128;
+    return p;
+  }
+  const int64_t base = z.heads * (p.n_qtiles > 0 ? p.n_qtiles : 1);
+  const int64_t max_split = (s->n_key + 127) / 128;
+  int64_t want = (2048 + base - 1) / base;
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  int64_t len = (s->n_key + want - 1) / want;
+  len = ((len + 127) / 128) * 128;
+  p.split_len = len;
+  p.nsplit = (int)((s->n_key + len - 1) / len);
+  return p;
+}
+
+struct RetrieveWs {
+  size_t part_s, part_i, total;
+};
+
+RetrieveWs retrieve_ws(const gca_shape* s, const Sizes& z, const gca::ScanPlan& p) {
+  RetrieveWs w{0, 0, 0};
+  if (p.nsplit <= 1) return w;
+  const size_t n = (size_t)z.q_rows * (size_t)p.nsplit * (size_t)p.kmax;
+  w.part_s = 0;
+  w.part_i = align_up(n * sizeof(float));
+  w.total = w.part_i + align_up(n * sizeof(int32_t));
+  (void)s;
+  return w;
+}
+
+struct BackwardWs {
+  size_t delta, rev_off, rev_ent, total;
+};
+
+BackwardWs backward_ws(const gca_shape* s, const Sizes& z) {
+  BackwardWs w{};
+  w.delta = 0;
+  w.rev_off = align_up((size_t)z.slots * (size_t)s->chunk_size * sizeof(float));
+  w.rev_ent = w.rev_off + align_up((size_t)z.heads * (size_t)(s->n_key + 1) * sizeof(int32_t));
+  w.total = w.rev_ent + align_up((size_t)z.slots * sizeof(int32_t));
+  return w;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+gca_status need(const void* p, const char* name, size_t align) {
+  if (p == nullptr) return fail(GCA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned(p, align))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, align);
+  return GCA_OK;
+}
+
+gca_status opt(const void* p, const char* name, size_t align) {
+  if (p != nullptr && !aligned(p, align))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, align);
+  return GCA_OK;
+}
+
+#define GCA_TRY(expr)                 \
+  do {                                \
+    gca_status st_ = (expr);          \
+    if (st_ != GCA_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int gca_abi_version(void) { return GCA_ABI_VERSION; }
+
+const char* gca_status_string(gca_status status) {
+  switch (status) {
+    case GCA_OK: return "GCA_OK";
+    case GCA_ERR_INVALID_ARGUMENT: return "GCA_ERR_INVALID_ARGUMENT";
+    case GCA_ERR_UNSUPPORTED: return "GCA_ERR_UNSUPPORTED";
+    case GCA_ERR_WORKSPACE: return "GCA_ERR_WORKSPACE";
+    case GCA_ERR_DEVICE: return "GCA_ERR_DEVICE";
+    default: return "GCA_UNKNOWN_STATUS";
+  }
+}
+
+const char* gca_last_error(void) { return g_err; }
+
+gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes) {
+  if (bytes == nullptr) return fail(GCA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (op < 0 || op > 2) return fail(GCA_ERR_INVALID_ARGUMENT, "op must be 0, 1 or 2");
+  Sizes z;
+  GCA_TRY(check_shape(shape, op, &z));
+  if (op == kRetrieve)
+    *bytes = retrieve_ws(shape, z, plan_scan(shape, z)).total;
+  else if (op == kForward)
+    *bytes = 0;
+  else
+    *bytes = backward_ws(shape, z).total;
+  g_err[0] = '\0';
+  return GCA_OK;
+}
+
+gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
+                        const int32_t* q_pos, int32_t* idx, float* score, float* w, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Sizes z;
+  GCA_TRY(check_shape(shape, kRetrieve, &z));
+  if (z.q_rows == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  GCA_TRY(need(lq, "lq", 16));
+  if (shape->n_key > 0) GCA_TRY(need(lk, "lk", 16));
+  GCA_TRY(need(q_pos, "q_pos", 4));
+  GCA_TRY(need(idx, "idx", 4));
+  GCA_TRY(need(score, "score", 4));
+  GCA_TRY(need(w, "w", 4));
+  const gca::ScanPlan plan = plan_scan(shape, z);
+  const RetrieveWs wl = retrieve_ws(shape, z, plan);
+  if (wl.total > 0) {
+    if (ws == nullptr || ws_bytes < wl.total)
+      return fail(GCA_ERR_WORKSPACE, "gca_retrieve needs %zu workspace bytes, got %zu",
+                  wl.total, ws == nullptr ? (size_t)0 : ws_bytes);
+    if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
+  }
+  const int64_t nblk = shape->dtype == GCA_BF16
+                           ? z.heads * plan.nsplit * (int64_t)plan.n_qtiles
+                           : (z.q_rows + 63) / 64;
+  if (nblk > 0x7fffffffLL) return fail(GCA_ERR_UNSUPPORTED, "retrieval grid too large");
+  gca::LaunchRetrieve a{};
+  a.G = shape->G;
+  a.B = shape->B;
+  a.H = shape->H;
+  a.n_query = shape->n_query;
+  a.n_key = shape->n_key;
+  a.dl = shape->landmark_dim;
+  a.k = shape->top_k;
+  a.dtype = shape->dtype;
+  a.softmax_one = shape->softmax_one;
+  a.score_scale = shape->score_scale;
+  a.lq = lq;
+  a.lk = lk;
+  a.q_pos = q_pos;
+  a.idx = idx;
+  a.score = score;
+  a.w = w;
+  a.part_s = wl.total ? (float*)((char*)ws + wl.part_s) : nullptr;
+  a.part_i = wl.total ? (int32_t*)((char*)ws + wl.part_i) : nullptr;
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_retrieve(plan, a), a.stream, "gca_retrieve");
+}
+
+gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
+  Sizes z;
+  GCA_TRY(check_shape(shape, kForward, &z));
+  if (z.q_rows == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  GCA_TRY(need(q, "q", 16));
+  if (shape->n_key > 0) {
+    GCA_TRY(need(k, "k", 16));
+    GCA_TRY(need(v, "v", 16));
+  }
+  GCA_TRY(need(idx, "idx", 4));
+  GCA_TRY(need(w, "w", 4));
+  GCA_TRY(need(o, "o", 16));
+  GCA_TRY(opt(lse, "lse", 4));
+  gca::LaunchForward a{};
+  a.G = shape->G;
+  a.B = shape->B;
+  a.H = shape->H;
+  a.n_query = shape->n_query;
+  a.n_key = shape->n_key;
+  a.S = shape->chunk_size;
+  a.D = shape->head_dim;
+  a.k = shape->top_k;
+  a.dtype = shape->dtype;
+  a.attn_scale = shape->attn_scale;
+  a.q = q;
+  a.kk = k;
+  a.v = v;
+  a.idx = idx;
+  a.w = w;
+  a.o = o;
+  a.lse = lse;
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_forward(a), a.stream, "gca_forward");
+}
+
+gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const float* w, const float* lse, const void* dout,
+                        const void* lq, const void* lk, void* dq, void* dk, void* dv, float* dw,
+                        float* dscore, float* dlq, float* dlk, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Sizes z;
+  GCA_TRY(check_shape(shape, kBackward, &z));
+  if (z.q_rows == 0 && z.k_rows == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  if (z.q_rows > 0) {
+    GCA_TRY(need(q, "q", 16));
+    GCA_TRY(need(dout, "dout", 16));
+    GCA_TRY(need(idx, "idx", 4));
+    GCA_TRY(need(w, "w", 4));
+    GCA_TRY(need(lse, "lse", 4));
+    GCA_TRY(need(dq, "dq", 16));
+    GCA_TRY(need(dw, "dw", 4));
+    GCA_TRY(need(dscore, "dscore", 4));
+  }
+  if (z.k_rows > 0) {
+    GCA_TRY(need(k, "k", 16));
+    GCA_TRY(need(v, "v", 16));
+    GCA_TRY(need(dk, "dk", 16));
+    GCA_TRY(need(dv, "dv", 16));
+  }
+  GCA_TRY(opt(dlq, "dlq", 4));
+  GCA_TRY(opt(dlk, "dlk", 4));
+  if (dlq != nullptr && z.q_rows > 0) GCA_TRY(need(lk, "lk (needed for dlq)", 16));
+  if (dlk != nullptr && z.k_rows > 0) GCA_TRY(need(lq, "lq (needed for dlk)", 16));
+  GCA_TRY(opt(lq, "lq", 16));
+  GCA_TRY(opt(lk, "lk", 16));
+  const BackwardWs wl = backward_ws(shape, z);
+  if (ws == nullptr || ws_bytes < wl.total)
+    return fail(GCA_ERR_WORKSPACE, "gca_backward needs %zu workspace bytes, got %zu", wl.total,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
+  gca::LaunchBackward a{};
+  a.G = shape->G;
+  a.B = shape->B;
+  a.H = shape->H;
+  a.n_query = shape->n_query;
+  a.n_key = shape->n_key;
+  a.S = shape->chunk_size;
+  a.D = shape->head_dim;
+  a.dl = shape->landmark_dim;
+  a.k = shape->top_k;
+  a.dtype = shape->dtype;
+  a.attn_scale = shape->attn_scale;
+  a.score_scale = shape->score_scale;
+  a.q = q;
+  a.kk = k;
+  a.v = v;
+  a.idx = idx;
+  a.w = w;
+  a.lse = lse;
+  a.dout = dout;
+  a.lq = dlk ? lq : nullptr;
+  a.lk = dlq ? lk : nullptr;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = dw;
+  a.dscore = dscore;
+  a.dlq = dlq;
+  a.dlk = dlk;
+  a.delta = (float*)((char*)ws + wl.delta);
+  a.rev_off = (int32_t*)((char*)ws + wl.rev_off);
+  a.rev_ent = (int32_t*)((char*)ws + wl.rev_ent);
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_backward(a), a.stream, "gca_backward");
+}
+
+}  // extern "C"

@@ -1,0 +1,222 @@
+// GCA forward: Eq. 2 per-chunk attention and Eq. 3 weighted fusion.
+//
+// Definition (long-context-modeling README, "Model Architecture"; paperlayer.ai
+// summary, section 3.1 and appendix B): every token x of query chunk t attends
+// separately to the S tokens of each retrieved chunk c_i, giving O^i[x] and the
+// log-sum-exp L_i[x]; the output is O[x] = sum_i w_i O^i[x].
+//
+// bf16 path (S = D = 64).  One workgroup of two waves per query chunk; wave w
+// owns query rows 32w .. 32w+31.  Per retrieved chunk:
+//   1. the K and V tiles (8 KB each) are copied into LDS with 16-byte loads;
+//   2. S^T = K Q^T on MFMA (A = K rows from LDS, B = Q^T kept in registers), so a
+//      lane holds 32 of the 64 logits of ONE query row and the partner lane
+//      (l ^ 32) the other 32: the row max and row sum need one exchange;
+//   3. p = exp2((s - max) * attn_scale * log2 e), l = sum p,
+//      L = attn_scale * max + ln l;
+//   4. the fusion weight is folded into the probabilities, p * (w_i / l), which
+//      become the B operand of O^T += V^T P^T directly from the S^T registers,
+//      so all k slots accumulate into ONE float32 accumulator.  Each chunk's
+//      softmax is complete inside one 64-key tile: no running rescale is needed.
+// O is rounded to bf16 once at the end.
+//
+// f32 path.  One thread per query row, float32 throughout (small workloads).
+
+#include "gca_device.h"
+#include "gca_launch.h"
+
+namespace gca {
+
+constexpr int kLdsStride = 72;  // bf16 per LDS tile row: 64 + 8 pad (conflict-free b128 reads)
+
+// Copies one 64 x 64 bf16 tile (row-major, 128 B rows) into LDS with 16-byte
+// loads; `nthreads` threads cooperate.
+template <int NTHREADS>
+__device__ __forceinline__ void tile_to_lds(bf16* dst, const bf16* __restrict__ src, int tid) {
+#pragma unroll
+  for (int r = 0; r < 512 / NTHREADS; ++r) {
+    const int ch = tid + NTHREADS * r;
+    const int row = ch >> 3, c8 = (ch & 7) * 8;
+    *(bf16x8*)(dst + row * kLdsStride + c8) = *(const bf16x8*)(src + row * 64 + c8);
+  }
+}
+
+__global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
+    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ o,
+    float* __restrict__ lse, int64_t n_query, int64_t n_key, int topk, float attn_scale) {
+  __shared__ bf16 k_lds[64 * kLdsStride];
+  __shared__ bf16 v_lds[64 * kLdsStride];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
+  const int64_t head = tile / n_query;
+  const int x = 32 * wave + col;  // query row owned by this lane
+
+  bf16x8 bq[4];  // Q^T as the B operand: column x, dims 32*half + 8*ks + 0..7
+  {
+    const bf16* row = q + tile * 4096 + x * 64 + 32 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bq[ks] = *(const bf16x8*)(row + 8 * ks);
+  }
+  f32x16 oacc[2] = {zero16(), zero16()};
+  const float c2 = attn_scale * kLog2e;
+
+  for (int i = 0; i < topk; ++i) {
+    const int c = idx[tile * topk + i];
+    const float wi = w[tile * topk + i];
+    float* lse_row = lse ? lse + (tile * topk + i) * 64 : nullptr;
+    if (c < 0 || c >= n_key) {
+      if (lse_row && half == 0) lse_row[x] = -__builtin_huge_valf();
+      continue;
+    }
+    const bf16* kt = kk + (head * n_key + c) * 4096;
+    const bf16* vt = v + (head * n_key + c) * 4096;
+    __syncthreads();  // the previous slot is done with the LDS tiles
+    tile_to_lds<128>(k_lds, kt, tid);
+    tile_to_lds<128>(v_lds, vt, tid);
+    __syncthreads();
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(k_lds + (32 * mt + col) * kLdsStride + 32 * half + 8 * ks);
+        sacc[mt] = mfma32x32x16(a, bq[ks], sacc[mt]);
+      }
+    }
+    float m = sacc[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[mt][r]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mb = m * c2;
+    float l = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(sacc[mt][r], c2, -mb));
+        sacc[mt][r] = e;
+        l += e;
+      }
+    l += __shfl_xor(l, 32);
+    if (lse_row && half == 0) lse_row[x] = attn_scale * m + logf(l);
+    const float ps = wi / l;
+
+    // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step ks covers keys
+    // 16ks + 4*half + 0..3 and 16ks + 8 + 4*half + 0..3, which are exactly the
+    // rows of S^T this lane holds in registers 4*g .. 4*g+3 for g = 2(ks&1),
+    // 2(ks&1)+1 of key tile ks/2.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mt = ks >> 1, g0 = 2 * (ks & 1);
+      bf16x8 bp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bp[e] = (bf16)(sacc[mt][4 * g0 + e] * ps);
+        bp[4 + e] = (bf16)(sacc[mt][4 * g0 + 4 + e] * ps);
+      }
+      const int j0 = 16 * ks + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        bf16x8 av;
+        const bf16* vc = v_lds + 32 * dt + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[e] = vc[(j0 + e) * kLdsStride];
+          av[4 + e] = vc[(j0 + 8 + e) * kLdsStride];
+        }
+        oacc[dt] = mfma32x32x16(av, bp, oacc[dt]);
+      }
+    }
+  }
+  // O[x][d]: this lane holds d = 32dt + 8g + 4*half + 0..3 for its row x.
+  bf16* orow = o + tile * 4096 + x * 64;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (bf16)oacc[dt][4 * g + e];
+      *(bf16x4*)(orow + 32 * dt + 8 * g + 4 * half) = val;
+    }
+}
+
+// float32 path: 64 threads per query chunk, thread x owns query row x (< S).
+__global__ __launch_bounds__(64) void k_fwd_f32(
+    const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ w, float* __restrict__ o,
+    float* __restrict__ lse, int64_t n_query, int64_t n_key, int S, int D, int topk,
+    float attn_scale) {
+  __shared__ float kt[64 * 64];
+  __shared__ float vt[64 * 64];
+  __shared__ float pr[64 * 65];
+  const int x = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  const int64_t head = tile / n_query;
+  const int64_t tsz = (int64_t)S * D;
+  float* orow = o + tile * tsz + (int64_t)x * D;
+  const float* qrow = q + tile * tsz + (int64_t)x * D;
+  if (x < S)
+    for (int d = 0; d < D; ++d) orow[d] = 0.0f;
+  for (int i = 0; i < topk; ++i) {
+    const int c = idx[tile * topk + i];
+    const float wi = w[tile * topk + i];
+    float* lse_row = lse ? lse + (tile * topk + i) * S : nullptr;
+    if (c < 0 || c >= n_key) {
+      if (lse_row && x < S) lse_row[x] = -__builtin_huge_valf();
+      continue;
+    }
+    __syncthreads();
+    const float* ks = kk + (head * n_key + c) * tsz;
+    const float* vs = v + (head * n_key + c) * tsz;
+    for (int e = x; e < S * D; e += 64) {
+      kt[e] = ks[e];
+      vt[e] = vs[e];
+    }
+    __syncthreads();
+    if (x < S) {
+      float* p = pr + x * 65;
+      float m = -__builtin_huge_valf();
+      for (int j = 0; j < S; ++j) {
+        float acc = 0.0f;
+        for (int d = 0; d < D; ++d) acc = fmaf(qrow[d], kt[j * D + d], acc);
+        p[j] = acc * attn_scale;
+        m = fmaxf(m, p[j]);
+      }
+      float l = 0.0f;
+      for (int j = 0; j < S; ++j) {
+        p[j] = expf(p[j] - m);
+        l += p[j];
+      }
+      if (lse_row) lse_row[x] = m + logf(l);
+      const float sc = wi / l;
+      for (int d = 0; d < D; ++d) {
+        float acc = 0.0f;
+        for (int j = 0; j < S; ++j) acc = fmaf(p[j], vt[j * D + d], acc);
+        orow[d] += sc * acc;
+      }
+    }
+  }
+}
+
+hipError_t launch_forward(const LaunchForward& a) {
+  const int64_t tiles = a.G * a.B * a.H * a.n_query;
+  if (tiles == 0) return hipSuccess;
+  if (a.dtype == 1) {
+    hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(128), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
+                       (bf16*)a.o, a.lse, a.n_query, a.n_key, a.k, a.attn_scale);
+  } else {
+    hipLaunchKernelGGL(k_fwd_f32, dim3((unsigned)tiles), dim3(64), 0, a.stream,
+                       (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.idx, a.w,
+                       (float*)a.o, a.lse, a.n_query, a.n_key, a.S, a.D, a.k, a.attn_scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gca

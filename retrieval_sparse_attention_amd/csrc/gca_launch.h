@@ -1,0 +1,78 @@
+// Internal launch interface between the C ABI (gca_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gca {
+
+// How the retrieval scan is cut into workgroups (chosen on the host, shared by
+// gca_workspace_size and gca_retrieve so both agree).
+struct ScanPlan {
+  int kmax;          // register list length: 4, 8 or 16 (>= k)
+  int n_qtiles;      // ceil(n_query / 32)
+  int nsplit;        // candidate slices per (head, query tile)
+  int64_t split_len; // candidates per slice (multiple of 128)
+};
+
+struct LaunchRetrieve {
+  int64_t G, B, H, n_query, n_key;
+  int dl, k, dtype, softmax_one;
+  float score_scale;
+  const void* lq;
+  const void* lk;
+  const int32_t* q_pos;
+  int32_t* idx;
+  float* score;
+  float* w;
+  float* part_s;    // [heads * n_query * nsplit * kmax] when nsplit > 1
+  int32_t* part_i;  // same
+  hipStream_t stream;
+};
+
+struct LaunchForward {
+  int64_t G, B, H, n_query, n_key;
+  int S, D, k, dtype;
+  float attn_scale;
+  const void* q;
+  const void* kk;
+  const void* v;
+  const int32_t* idx;
+  const float* w;
+  void* o;
+  float* lse;
+  hipStream_t stream;
+};
+
+struct LaunchBackward {
+  int64_t G, B, H, n_query, n_key;
+  int S, D, dl, k, dtype;
+  float attn_scale, score_scale;
+  const void* q;
+  const void* kk;
+  const void* v;
+  const int32_t* idx;
+  const float* w;
+  const float* lse;
+  const void* dout;
+  const void* lq;
+  const void* lk;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw;
+  float* dscore;
+  float* dlq;
+  float* dlk;
+  float* delta;      // workspace [heads * n_query * k * S]: rowsum(P * dP) per pair
+  int32_t* rev_off;  // workspace [heads * (n_key + 1)]
+  int32_t* rev_ent;  // workspace [heads * n_query * k]: q * k + slot, grouped by chunk
+  hipStream_t stream;
+};
+
+hipError_t launch_retrieve(const ScanPlan& plan, const LaunchRetrieve& a);
+hipError_t launch_forward(const LaunchForward& a);
+hipError_t launch_backward(const LaunchBackward& a);
+
+}  // namespace gca

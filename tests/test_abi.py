@@ -1,0 +1,127 @@
+"""C-ABI boundary on the host: the library loads, exports what include/gca.h
+declares, and rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import retrieval_sparse_attention_amd as gca
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gca.h")
+P = ctypes.c_void_p
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gca_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = gca.load()
+    names = _declared()
+    assert set(names) == set(gca.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert gca.gca_abi_version() == 1
+    assert gca.gca_status_string(0) == "GCA_OK"
+    assert gca.gca_status_string(3) == "GCA_ERR_WORKSPACE"
+    assert gca.gca_status_string(99) == "GCA_UNKNOWN_STATUS"
+
+
+def _bf16_shape(**over):
+    s = dict(G=2, B=4, H=12, n_query=256, n_key=256, chunk_size=64, head_dim=64,
+             landmark_dim=64, top_k=8, dtype=gca.GCA_BF16, softmax_one=1)
+    s.update(over)
+    return gca.make_shape(**s)
+
+
+def _status(fn, *args):
+    lib = gca.load()
+    return getattr(lib, fn)(*args), gca.gca_last_error()
+
+
+def test_workspace_sizes():
+    s = _bf16_shape()
+    assert gca.gca_workspace_size(s, gca.OP_FORWARD) == 0
+    # delta: 96 heads * 256 * 8 * 64 floats; rev_off: 96 * 257 ints; rev_ent: 96 * 2048 ints
+    expect = 96 * 256 * 8 * 64 * 4 + ((96 * 257 * 4 + 255) // 256) * 256 + 96 * 2048 * 4
+    assert gca.gca_workspace_size(s, gca.OP_BACKWARD) == expect
+    assert gca.gca_workspace_size(s, gca.OP_RETRIEVE) == 0  # 256 candidates: one slice
+    big = _bf16_shape(G=1, B=1, n_query=32, n_key=262144, softmax_one=0)
+    assert gca.gca_workspace_size(big, gca.OP_RETRIEVE) > 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(n_key=-1), 1), (dict(top_k=0), 1), (dict(top_k=17), 2),
+    (dict(dtype=7), 1), (dict(softmax_one=2), 1), (dict(chunk_size=32), 2),
+    (dict(head_dim=128), 2), (dict(landmark_dim=48), 2), (dict(n_key=2 ** 31), 1),
+    (dict(attn_scale=float("inf")), 1),
+])
+def test_bad_shapes(over, code):
+    s = _bf16_shape(**over)
+    n = ctypes.c_size_t(0)
+    st, msg = _status("gca_workspace_size", ctypes.byref(s), 2, ctypes.byref(n))
+    assert st == code and msg
+
+
+def test_f32_limits():
+    ok = _bf16_shape(dtype=gca.GCA_F32, chunk_size=16, head_dim=32, landmark_dim=128)
+    assert gca.gca_workspace_size(ok, gca.OP_BACKWARD) > 0
+    bad = _bf16_shape(dtype=gca.GCA_F32, chunk_size=65)
+    n = ctypes.c_size_t(0)
+    assert _status("gca_workspace_size", ctypes.byref(bad), 1, ctypes.byref(n))[0] == 2
+
+
+def test_null_shape_and_op():
+    n = ctypes.c_size_t(0)
+    assert _status("gca_workspace_size", None, 0, ctypes.byref(n))[0] == 1
+    s = _bf16_shape()
+    assert _status("gca_workspace_size", ctypes.byref(s), 5, ctypes.byref(n))[0] == 1
+    assert _status("gca_workspace_size", ctypes.byref(s), 0, None)[0] == 1
+
+
+# Fake device addresses: the calls below must fail in validation, before any
+# HIP call, so these are never dereferenced.
+A = P(0x7f0000000000)
+MIS = P(0x7f0000000002)
+
+
+def test_forward_rejects_null_and_misaligned():
+    s = _bf16_shape()
+    st, msg = _status("gca_forward", ctypes.byref(s), None, A, A, A, A, A, None, None)
+    assert st == 1 and "q is NULL" in msg
+    st, msg = _status("gca_forward", ctypes.byref(s), MIS, A, A, A, A, A, None, None)
+    assert st == 1 and "aligned" in msg
+    st, msg = _status("gca_forward", ctypes.byref(s), A, A, A, A, A, None, None, None)
+    assert st == 1 and "o is NULL" in msg
+
+
+def test_retrieve_needs_workspace_when_sliced():
+    s = _bf16_shape(G=1, B=1, n_query=32, n_key=262144, softmax_one=0)
+    st, msg = _status("gca_retrieve", ctypes.byref(s), A, A, A, A, A, A, None,
+                      ctypes.c_size_t(0), None)
+    assert st == 3 and "workspace" in msg
+
+
+def test_backward_rejects_small_workspace_and_missing_landmarks():
+    s = _bf16_shape()
+    need = gca.gca_workspace_size(s, gca.OP_BACKWARD)
+    args = [A] * 14
+    st, msg = _status("gca_backward", ctypes.byref(s), *args, A, A, A, ctypes.c_size_t(need - 1),
+                      None)
+    assert st == 3
+    # dlk requested without lq
+    args = [A, A, A, A, A, A, A, None, A, A, A, A, A, A, A, A]
+    st, msg = _status("gca_backward", ctypes.byref(s), *args, A, ctypes.c_size_t(need), None)
+    assert st == 1 and "lq" in msg
+
+
+def test_empty_problem_is_a_no_op():
+    s = _bf16_shape(n_query=0, n_key=0)
+    assert _status("gca_forward", ctypes.byref(s), None, None, None, None, None, None, None,
+                   None)[0] == 0

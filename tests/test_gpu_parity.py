@@ -1,0 +1,153 @@
+"""GPU parity of the GCA library against the float64 oracle (needs an MI355X).
+
+Every test feeds the same seeded inputs to both sides.  Top-k indices must be
+bit-identical; values must meet the tolerances: float32 workloads 1e-5
+max-abs; bf16 workloads 2e-2 max-abs and 1e-2 mean-relative (mean |gpu - ref| /
+mean |ref| per tensor), with float32 accumulation on the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gca_oracle as orc
+from gpu_common import (accept_for, close, compare_lse, dev, f64, require_gpu, run_backward,
+                        run_forward, run_retrieve, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _full_path(name, heads=None, **over):
+    """retrieve -> forward -> backward on the GPU and in the oracle; all compared."""
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
+    bf = cfg["dtype"] == "bf16"
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    idx, score, w = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
+    lq64, lk64 = f64(x["lq"]), f64(x["lk"])
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, x["q_pos"].numpy(), cfg["k"],
+                                       cfg["score_scale"], cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx), "top-k indices differ"
+    close("score", f64(score), r_score, bf)
+    close("w", f64(w), r_w, bf)
+    o, lse = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
+    q64, k64, v64, do64 = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"])
+    r_o, r_lse = orc.forward(q64, k64, v64, r_idx, r_w, cfg["attn_scale"])
+    close("o", f64(o), r_o, bf)
+    compare_lse(lse, r_lse, bf)
+    g = run_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"])
+    r = orc.backward(q64, k64, v64, r_idx, r_w, do64, lq64, lk64, cfg["attn_scale"],
+                     cfg["score_scale"], heads=heads)
+    if heads is None:
+        for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+            close(key, f64(g[key]), r[key], bf)
+    else:
+        for (gg, b, h) in heads:
+            for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+                close(f"{key}[{gg},{b},{h}]", f64(g[key][gg, b, h]), r[key][gg, b, h], bf)
+    return g
+
+
+def test_tiny_fp32_full_path():
+    _full_path("tiny_fp32")
+
+
+def test_tiny_fp32_ragged_and_k3():
+    # 21 chunks of 5 tokens, D=7, Dl=9, top-3: nothing is a power of two
+    _full_path("tiny_fp32", n_query=21, n_key=21, S=5, D=7, Dl=9, k=3, H=3, softmax_one=1)
+
+
+def test_bf16_small_vanilla_aliased():
+    # 40 query chunks: one full 32-query tile plus a ragged tail of 8
+    _full_path("train16k_fwd", B=1, H=3, n_query=40, n_key=40)
+
+
+def test_bf16_small_off_by_one_two_groups():
+    _full_path("train16k_fwdbwd_g2", B=2, H=2, n_query=72, n_key=72)
+
+
+@pytest.mark.parametrize("k", [1, 5, 16])
+def test_bf16_top_k_sizes(k):
+    _full_path("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=48, n_key=48, k=k)
+
+
+def test_bf16_landmark_dim_32():
+    _full_path("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=40, n_key=40, Dl=32)
+
+
+def test_bf16_sliced_scan_with_needles():
+    """n_key > 1024 takes the sliced scan + merge path; planted needles rank 1."""
+    over = dict(n_key=5000, n_query=37, H=2, q_pos=5001)
+    cfg = synth.workload("retrieve16m", **over)
+    lk = synth.context_landmarks("retrieve16m", **over)
+    qb = synth.query_batch("retrieve16m", lk, accept=accept_for(cfg), **over)
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(qb["lq"]), dev(lk), dev(qb["q_pos"]))
+    r_idx, r_score, r_w = orc.retrieve(f64(qb["lq"]), f64(lk), qb["q_pos"].numpy(), cfg["k"],
+                                       cfg["score_scale"], cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    close("score", f64(score), r_score, True)
+    close("w", f64(w), r_w, True)
+    best = np.take_along_axis(r_idx, np.argmax(r_score, axis=-1)[..., None], -1)[..., 0]
+    assert (best == qb["needle"].numpy()[None, None, None, :]).all()
+
+
+def test_bf16_edge_positions():
+    """q_pos giving 0, fewer than k, exactly k and all candidates; n_key not a multiple of 32."""
+    cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=6, n_key=45)
+    rng = np.random.default_rng(4)
+    lq = torch.from_numpy(rng.standard_normal((1, 1, 2, 6, 64)).astype(np.float32) / 8).bfloat16()
+    lk = torch.from_numpy(rng.standard_normal((1, 1, 2, 45, 64)).astype(np.float32) / 8).bfloat16()
+    q_pos = torch.tensor([0, 1, 4, 9, 46, 1000], dtype=torch.int32)
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(lq), dev(lk), dev(q_pos))
+    r_idx, r_score, r_w = orc.retrieve(f64(lq), f64(lk), q_pos.numpy(), cfg["k"],
+                                       cfg["score_scale"], cfg["softmax_one"])
+    # no near-ties here: the k-th gaps of these draws exceed the float32 score error
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    close("score", f64(score), r_score, True)
+    close("w", f64(w), r_w, True)
+
+
+def test_bf16_forward_invalid_and_duplicate_slots():
+    """Slots with idx -1 or >= n_key are empty; a duplicated chunk counts twice."""
+    cfg = synth.workload("train16k_fwd", B=1, H=1, n_query=4, n_key=9)
+    x = synth.training_inputs("train16k_fwd", B=1, H=1, n_query=4, n_key=4)
+    rng = np.random.default_rng(8)
+    k = torch.from_numpy(rng.standard_normal((1, 1, 1, 9, 64, 64)).astype(np.float32) / 8).bfloat16()
+    v = torch.from_numpy(rng.standard_normal((1, 1, 1, 9, 64, 64)).astype(np.float32) / 8).bfloat16()
+    idx = torch.tensor([[[[[3, -1, 7, 9, 2, 2, 100, 0],
+                          [-1] * 8,
+                          [0, 1, 2, 3, 4, 5, 6, 8],
+                          [8, 7, 6, 5, 4, 3, 2, 1]]]]], dtype=torch.int32)
+    w = torch.from_numpy(rng.random((1, 1, 1, 4, 8)).astype(np.float32))
+    shape = shape_of(cfg)
+    o, lse = run_forward(shape, dev(x["q"]), dev(k), dev(v), dev(idx), dev(w))
+    r_o, r_lse = orc.forward(f64(x["q"]), f64(k), f64(v), idx.numpy(), w.numpy().astype(np.float64),
+                             cfg["attn_scale"])
+    close("o", f64(o), r_o, True)
+    compare_lse(lse, r_lse, True)
+    assert (f64(o)[0, 0, 0, 1] == 0).all()
+
+
+def test_bf16_backward_is_deterministic():
+    cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=64, n_key=64)
+    x = synth.training_inputs("train16k_fwdbwd_g2", accept=accept_for(cfg), G=1, B=1, H=2,
+                              n_query=64, n_key=64)
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    idx, score, w = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
+    o, lse = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
+    g1 = run_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"])
+    g2 = run_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"])
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+    o2, lse2 = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
