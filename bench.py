@@ -1,0 +1,262 @@
+"""Benchmark of the GCA hot path on one MI355X.
+
+One step = one training pass of one upper layer's Grouped Cross Attention over
+a 16K-token batch: gca_retrieve (landmark scan, top-8, fusion weights) +
+gca_forward (per-chunk attention and fusion) + gca_backward (dQ, dK, dV, dw,
+dscore, d landmarks), for G=2 retrieval groups with softmax off-by-one, B=4,
+H=12, 16384 tokens = 256 chunks of 64, head/landmark dim 64, bf16 inputs with
+float32 accumulation.  Inputs are seeded synthetic tensors resident in HBM.
+
+Prints ONE JSON line: tokens/s of the whole step, the roofline position of the
+dominant kernel (per-kernel HIP-event timing inside the timed region) and the
+float64 oracle timed on a bounded sample on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--cpu-heads N]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+MFMA_BF16_PEAK = 2.5e15    # MI355X dense bf16 MFMA, flop/s
+WORKLOAD = "train16k_fwdbwd_g2"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=12,
+                    help="(g, b, h) heads of one step the oracle runs for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="BYTES",
+                    help="after the timed steps, one device-to-device copy of BYTES "
+                         "(reference dispatch for scaling hardware byte counters)")
+    return ap.parse_args()
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "retrieval_sparse_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(cfg, pairs):
+    """Algorithmic HBM bytes and flops of one launch of each kernel.
+
+    Bytes count every tensor the kernel must read or write once (gathered K/V
+    tiles that are re-read from cache are not counted again); flops count the
+    tile products the kernel must form given its inputs (2*S*S*D each).
+    """
+    G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
+    S, D, Dl, k = cfg["S"], cfg["D"], cfg["Dl"], cfg["k"]
+    heads = G * B * H
+    tile = S * D * 2                       # one bf16 chunk tile
+    qt, kt = heads * Nq * tile, heads * Nk * tile
+    slots = heads * Nq * k
+    mm = 2 * S * S * D                      # one S x S x D product
+    cand = heads * sum(max(0, min(t - 1, Nk)) for t in range(Nq))
+    return {
+        "scan_topk": dict(bytes=heads * (Nq + Nk) * Dl * 2 + slots * 12 + Nq * 4,
+                          flops=2 * Dl * cand),
+        "forward": dict(bytes=qt + 2 * kt + qt + slots * S * 4 + slots * 8,
+                        flops=2 * mm * pairs),
+        "reverse_index": dict(bytes=slots * 8 + heads * (Nk + 1) * 4, flops=0),
+        "backward_q": dict(bytes=2 * qt + 2 * kt + qt + 2 * slots * S * 4 + slots * 16
+                           + heads * Nq * Dl * 4, flops=3 * mm * pairs),
+        "backward_kv": dict(bytes=2 * kt + 2 * qt + 2 * kt + 2 * slots * S * 4 + slots * 12
+                            + heads * Nk * Dl * 4, flops=4 * mm * pairs),
+    }
+
+
+def roofline_entry(name, avg_s, work):
+    t_hbm = work["bytes"] / HBM_PEAK
+    t_mfma = work["flops"] / MFMA_BF16_PEAK
+    if t_mfma >= t_hbm:
+        ach = work["flops"] / avg_s / 1e12
+        return dict(kernel=name, bound="mfma", achieved=round(ach, 2),
+                    peak=MFMA_BF16_PEAK / 1e12, unit="TFLOP/s",
+                    frac=round(ach / (MFMA_BF16_PEAK / 1e12), 4))
+    ach = work["bytes"] / avg_s / 1e9
+    return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK / 1e9,
+                unit="GB/s", frac=round(ach / (HBM_PEAK / 1e9), 4))
+
+
+def traffic_for(kernel, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}@{WORKLOAD}")
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, cfg, n_heads):
+    """The float64 oracle on `n_heads` (g, b, h) heads of one step, one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gca_oracle as orc
+    G, B, H = cfg["G"], cfg["B"], cfg["H"]
+    heads = [(g, b, h) for g in range(G) for b in range(B) for h in range(H)][:n_heads]
+    f = lambda t: t.to("cpu").double().numpy()
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for (g, b, h) in heads:
+            sl = lambda t: f(t[g:g + 1, b:b + 1, h:h + 1])
+            q, k, v, do = sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["dout"])
+            lq, lk = sl(x["lq"]), sl(x["lk"])
+            idx, _, w = orc.retrieve(lq, lk, x["q_pos"].numpy(), cfg["k"], cfg["score_scale"],
+                                     cfg["softmax_one"])
+            orc.forward(q, k, v, idx, w, cfg["attn_scale"])
+            orc.backward(q, k, v, idx, w, do, lq, lk, cfg["attn_scale"], cfg["score_scale"])
+        dt = time.perf_counter() - t0
+    total_heads = G * B * H
+    step_s = dt * total_heads / len(heads)
+    tokens = cfg["B"] * cfg["n_query"] * cfg["S"]
+    return dict(value=round(tokens / step_s, 2), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{len(heads)} of {total_heads} (g,b,h) heads of one step "
+                       f"(retrieve+forward+backward, float64 numpy, BLAS limited to 1 thread), "
+                       f"{dt:.1f} s, scaled by {total_heads}/{len(heads)}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GCA hot path here runs on a single MI355X "
+              "(every (g, b, h) head is independent; see the design notes for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a ROCm GPU")
+    gca.load()
+    torch.cuda.set_device(0)
+    cfg = synth.workload(WORKLOAD)
+    x = synth.training_inputs(WORKLOAD)
+    d = {key: val.contiguous().cuda() for key, val in x.items() if key != "cfg"}
+    G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
+    S, D, Dl, k = cfg["S"], cfg["D"], cfg["Dl"], cfg["k"]
+    shape = gca.make_shape(G, B, H, Nq, Nk, S, D, Dl, k, gca.GCA_BF16, cfg["softmax_one"],
+                           cfg["attn_scale"], cfg["score_scale"])
+    dev = "cuda"
+    idx = torch.empty((G, B, H, Nq, k), dtype=torch.int32, device=dev)
+    score = torch.empty((G, B, H, Nq, k), dtype=torch.float32, device=dev)
+    w = torch.empty_like(score)
+    o = torch.empty_like(d["q"])
+    lse = torch.empty((G, B, H, Nq, k, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    dw, dscore = torch.empty_like(score), torch.empty_like(score)
+    dlq = torch.empty(tuple(d["lq"].shape), dtype=torch.float32, device=dev)
+    dlk = torch.empty(tuple(d["lk"].shape), dtype=torch.float32, device=dev)
+    ws_r = gca.gca_workspace_size(shape, gca.OP_RETRIEVE)
+    ws_b = gca.gca_workspace_size(shape, gca.OP_BACKWARD)
+    wsr = torch.empty(max(ws_r, 256), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], idx, score, w, ws=wsr)
+        gca.gca_forward(shape, d["q"], d["k"], d["v"], idx, w, o, lse)
+        gca.gca_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"],
+                         dq, dk, dv, dw, dscore, dlq, dlk, ws=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    gca.gca_timing_enable(True)
+    gca.gca_timing_collect()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gca.gca_timing_enable(False)
+    per_kernel = gca.gca_timing_collect()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    tokens = B * Nq * S
+    value = tokens / (step_ms / 1e3)
+    pairs = int((idx >= 0).sum().item())
+    work = kernel_work(cfg, pairs)
+    kernels = {}
+    for name, (tot, n) in per_kernel.items():
+        if n:
+            kernels[name] = dict(avg_us=round(tot / n * 1e3, 2), launches=n)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    roof = roofline_entry(dom, kernels[dom]["avg_us"] * 1e-6, work[dom])
+    digest = source_digest()
+    roof["traffic"] = traffic_for(dom, digest)
+    roof["algorithmic_bytes"] = work[dom]["bytes"]
+    roof["algorithmic_flops"] = work[dom]["flops"]
+    for name in kernels:
+        if name in work:
+            e = roofline_entry(name, kernels[name]["avg_us"] * 1e-6, work[name])
+            kernels[name].update(bound=e["bound"], frac=e["frac"])
+    print(f"[bench] timed {args.steps} steps: {step_ms:.3f} ms/step, dominant {dom}",
+          file=sys.stderr, flush=True)
+    if args.copy_ref > 0:
+        n = args.copy_ref // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy reference: {n} bytes read, {n} bytes written", file=sys.stderr,
+              flush=True)
+        del src, dst
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, cfg, args.cpu_heads)
+    line = {
+        "metric": "GCA fwd+bwd tokens/s @16K ctx k=8",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/8 q,k,v,landmarks; N(0,1) dO)",
+        "config": {"workload": WORKLOAD, "G": G, "B": B, "H": H, "tokens": Nq * S,
+                   "chunk_size": S, "head_dim": D, "landmark_dim": Dl, "top_k": k,
+                   "softmax_one": cfg["softmax_one"], "pairs": pairs,
+                   "step": "gca_retrieve + gca_forward + gca_backward"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+        "source_digest": digest,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,8 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *   never allocates or frees device memory and keeps no state except a
- *   thread-local error string.
+ *   never allocates or frees device memory.  Its only state is a thread-local
+ *   error string and, while enabled, the event timing records below.
  * - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *   return without synchronising.
  * - All arrays are dense, contiguous, row-major, with the layouts given below.
@@ -40,7 +40,8 @@
  * Supported sizes (anything else returns GCA_ERR_UNSUPPORTED):
  *   dtype GCA_BF16 : chunk_size 64, head_dim 64, landmark_dim 32 or 64
  *   dtype GCA_F32  : chunk_size 1..64, head_dim 1..64, landmark_dim 1..128
- *   top_k 1..16; gca_backward additionally needs n_query * top_k <= 16384.
+ *   top_k 1..16; n_key < 2^31 - 1; at most 2^31 - 1 query or key chunk tiles
+ *   (G*B*H*n_query, G*B*H*n_key); gca_backward needs n_query * top_k < 2^31.
  */
 #ifndef GCA_H
 #define GCA_H
@@ -193,6 +194,23 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k,
                         const void* lk, void* dq, void* dk, void* dv, float* dw,
                         float* dscore, float* dlq, float* dlk, void* ws,
                         size_t ws_bytes, void* stream);
+
+/*
+ * Per-kernel timing with HIP events (benchmarks, profiling).
+ *
+ * gca_timing_enable(1) makes every later call record a HIP event before and
+ * after each kernel it launches, on that call's stream (a small cost per
+ * launch); gca_timing_enable(0) stops recording.  gca_timing_collect() waits
+ * for the recorded events, then writes per-kernel sums since the previous
+ * collect into total_ms[i] (milliseconds) and launches[i] (count) for
+ * i < gca_num_kernels(), and resets the sums.  Either array may be NULL.
+ * Returns GCA_ERR_DEVICE if an event could not be read.  Thread-safe.
+ * gca_kernel_name(i) names kernel i ("" outside the range).
+ */
+int gca_num_kernels(void);
+const char* gca_kernel_name(int kernel_id);
+gca_status gca_timing_enable(int on);
+gca_status gca_timing_collect(double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 } /* extern "C" */

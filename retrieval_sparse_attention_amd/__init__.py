@@ -21,13 +21,15 @@ import os
 __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
            "gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "OP_RETRIEVE",
-           "OP_FORWARD", "OP_BACKWARD", "EXPORTED"]
+           "OP_FORWARD", "OP_BACKWARD", "EXPORTED", "gca_num_kernels", "gca_kernel_name",
+           "gca_timing_enable", "gca_timing_collect"]
 
 GCA_F32 = 0
 GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
-            "gca_retrieve", "gca_forward", "gca_backward")
+            "gca_retrieve", "gca_forward", "gca_backward", "gca_num_kernels", "gca_kernel_name",
+            "gca_timing_enable", "gca_timing_collect")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -87,6 +89,15 @@ def load():
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
     lib.gca_backward.restype = ctypes.c_int
     lib.gca_backward.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
+    lib.gca_num_kernels.restype = ctypes.c_int
+    lib.gca_num_kernels.argtypes = []
+    lib.gca_kernel_name.restype = ctypes.c_char_p
+    lib.gca_kernel_name.argtypes = [ctypes.c_int]
+    lib.gca_timing_enable.restype = ctypes.c_int
+    lib.gca_timing_enable.argtypes = [ctypes.c_int]
+    lib.gca_timing_collect.restype = ctypes.c_int
+    lib.gca_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int64)]
     _lib = lib
     return lib
 
@@ -163,3 +174,24 @@ def gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dsco
         _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"), _ptr(dw, "dw"), _ptr(dscore, "dscore"),
         _ptr(dlq, "dlq"), _ptr(dlk, "dlk"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_num_kernels():
+    return load().gca_num_kernels()
+
+
+def gca_kernel_name(kernel_id):
+    return load().gca_kernel_name(int(kernel_id)).decode()
+
+
+def gca_timing_enable(on):
+    _check(load().gca_timing_enable(1 if on else 0))
+
+
+def gca_timing_collect():
+    """{kernel name: (total_ms, launches)} since the previous collect."""
+    n = gca_num_kernels()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(load().gca_timing_collect(ms, cnt))
+    return {gca_kernel_name(i): (float(ms[i]), int(cnt[i])) for i in range(n)}

@@ -28,101 +28,105 @@
 
 namespace gca {
 
-constexpr int kLdsStrideB = 72;  // bf16 per LDS tile row (64 + 8 pad)
-
-template <int NTHREADS>
-__device__ __forceinline__ void tile64_to_lds(bf16* dst, const bf16* __restrict__ src, int tid) {
-#pragma unroll
-  for (int r = 0; r < 512 / NTHREADS; ++r) {
-    const int ch = tid + NTHREADS * r;
-    const int row = ch >> 3, c8 = (ch & 7) * 8;
-    *(bf16x8*)(dst + row * kLdsStrideB + c8) = *(const bf16x8*)(src + row * 64 + c8);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Reverse index.  One workgroup (256 threads, 4 waves) per head.
+// Reverse index.  One workgroup (512 threads, 8 waves) per head.
 // rev_off[head][c] .. rev_off[head][c+1] delimit the entries (t*k + i) of key
 // chunk c in rev_ent[head][...], in ascending entry order.  Out-of-range idx
-// values are skipped.  Stable counting sort: the entries are cut into 4
-// segments (one per wave); per pass over 512 key chunks, (segment, chunk)
-// counts give every segment its own write cursor per chunk, and lane l of wave
-// s appends, in entry order, the entries of segment s whose chunk is one of its
-// 8 chunks.  Integer counts only, so the result does not depend on timing.
+// values are skipped.  Stable counting sort with integer counts only:
+//   1. the entries are cut into 8 segments, one per wave; per pass over 512
+//      key chunks each wave counts the chunks of its segment (LDS atomics);
+//   2. an exclusive scan over (chunk, segment) gives every segment its own
+//      write cursor per chunk;
+//   3. each wave places its entries 64 at a time: a lane's rank among the
+//      earlier lanes with the same chunk comes from a compare loop over the
+//      64 chunk ids in LDS, so all lanes write in parallel and the order
+//      inside each list is the entry order.
 // ---------------------------------------------------------------------------
-constexpr int kRevKeys = 512;  // key chunks per pass = 64 lanes x 8
-constexpr int kRevSeg = 4;     // entry segments = waves
+constexpr int kRevWaves = 8;
+constexpr int kRevKeys = 512;  // key chunks per pass = threads per workgroup
 
-__global__ __launch_bounds__(256) void k_reverse_index(const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict__ idx,
                                                        int64_t n_query, int64_t n_key, int topk,
                                                        int32_t* __restrict__ rev_off,
                                                        int32_t* __restrict__ rev_ent) {
-  __shared__ int cnt[kRevSeg][kRevKeys];
-  __shared__ int part[256];
+  __shared__ int cnt[kRevWaves][kRevKeys];
+  __shared__ int part[kRevKeys];
+  __shared__ __align__(16) int kbuf[kRevWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t head = blockIdx.x;
-  const int64_t n_ent = n_query * topk;
-  const int64_t segsz = (n_ent + kRevSeg - 1) / kRevSeg;
-  const int32_t* ih = idx + head * n_ent;
+  const int n_ent = (int)(n_query * topk);  // < 2^31, checked on the host
+  const int nk = (int)n_key;
+  const int segsz = (n_ent + kRevWaves - 1) / kRevWaves;
+  const int32_t* ih = idx + head * (int64_t)n_ent;
   int32_t* off = rev_off + head * (n_key + 1);
-  int32_t* out = rev_ent + head * n_ent;
+  int32_t* out = rev_ent + head * (int64_t)n_ent;
+  const int e_beg = wave * segsz;
+  const int e_end = min(e_beg + segsz, n_ent);
   int base = 0;
-  for (int64_t c0 = 0; c0 < n_key; c0 += kRevKeys) {
-    const int nc = (int)((n_key - c0) < kRevKeys ? (n_key - c0) : kRevKeys);
-    for (int u = tid; u < kRevSeg * kRevKeys; u += 256) (&cnt[0][0])[u] = 0;
+  for (int c0 = 0; c0 < nk; c0 += kRevKeys) {
+    const int nc = min(kRevKeys, nk - c0);
+#pragma unroll
+    for (int w8 = 0; w8 < kRevWaves; ++w8) cnt[w8][tid] = 0;
     __syncthreads();
-    for (int64_t e = tid; e < n_ent; e += 256) {
-      const int64_t c = ih[e];
-      if (c >= c0 && c < c0 + nc) atomicAdd(&cnt[e / segsz][c - c0], 1);
+    for (int e0 = e_beg; e0 < e_end; e0 += 64 * 8) {
+      int kv[8];  // unconditional loads from clamped addresses: all in flight together
+#pragma unroll
+      for (int r = 0; r < 8; ++r) kv[r] = ih[min(e0 + 64 * r + lane, n_ent - 1)];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int rel = kv[r] - c0;
+        if (e0 + 64 * r + lane < e_end && rel >= 0 && rel < nc) atomicAdd(&cnt[wave][rel], 1);
+      }
     }
     __syncthreads();
-    // thread owns chunks 2*tid, 2*tid+1: totals, then a block-wide exclusive scan
-    int tot[2];
-    int sum = 0;
+    int tot = 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      int t = 0;
-#pragma unroll
-      for (int sg = 0; sg < kRevSeg; ++sg) t += cnt[sg][2 * tid + u];
-      tot[u] = t;
-      sum += t;
-    }
-    part[tid] = sum;
+    for (int w8 = 0; w8 < kRevWaves; ++w8) tot += cnt[w8][tid];
+    part[tid] = tot;
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
+    for (int o = 1; o < kRevKeys; o <<= 1) {
       const int add = tid >= o ? part[tid - o] : 0;
       __syncthreads();
       part[tid] += add;
       __syncthreads();
     }
-    const int total = part[255];
-    int run = base + part[tid] - sum;
+    const int total = part[kRevKeys - 1];
+    int cur = base + part[tid] - tot;
+    if (tid < nc) off[c0 + tid] = cur;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 2 * tid + u;
-      if (key < nc) off[c0 + key] = run;
-      int cur = run;
-#pragma unroll
-      for (int sg = 0; sg < kRevSeg; ++sg) {
-        const int cs = cnt[sg][key];
-        cnt[sg][key] = cur;  // becomes the write cursor of (segment, chunk)
-        cur += cs;
-      }
-      run += tot[u];
+    for (int w8 = 0; w8 < kRevWaves; ++w8) {
+      const int cs = cnt[w8][tid];
+      cnt[w8][tid] = cur;  // becomes the write cursor of (segment, chunk)
+      cur += cs;
     }
     __syncthreads();
-    int cur[8];
+    for (int e0 = e_beg; e0 < e_end; e0 += 64 * 8) {
+      int kv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) cur[u] = cnt[wave][lane * 8 + u];
-    const int64_t e_beg = wave * segsz;
-    const int64_t e_end = (e_beg + segsz) < n_ent ? (e_beg + segsz) : n_ent;
-    const int64_t my0 = c0 + lane * 8;
-    for (int64_t e = e_beg; e < e_end; ++e) {
-      const int64_t rel = (int64_t)ih[e] - my0;
-      if (rel >= 0 && rel < 8) {
+      for (int r = 0; r < 8; ++r) kv[r] = ih[min(e0 + 64 * r + lane, n_ent - 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (rel == u) out[cur[u]++] = (int)e;
+      for (int r = 0; r < 8; ++r) {
+        if (e0 + 64 * r >= e_end) break;  // wave-uniform
+        const int e = e0 + 64 * r + lane;
+        const int rel = kv[r] - c0;
+        const bool inr = e < e_end && rel >= 0 && rel < nc;
+        const int key = inr ? rel : -1 - lane;  // distinct negatives never match
+        kbuf[wave][lane] = key;
+        int rank = 0;
+        bool later = false;
+#pragma unroll
+        for (int l4 = 0; l4 < 64; l4 += 4) {
+          const int4 k4 = *(const int4*)&kbuf[wave][l4];
+          const int kk4[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool m = kk4[q] == key;
+            rank += (m && l4 + q < lane) ? 1 : 0;
+            later = later || (m && l4 + q > lane);
+          }
+        }
+        if (inr) out[cnt[wave][rel] + rank] = e;
+        if (inr && !later) cnt[wave][rel] += rank + 1;
       }
     }
     base += total;
@@ -154,8 +158,13 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
   if (dlq_row) {
     for (int d = tid; d < dl; d += nthreads) {
       float acc = 0.0f;
-      for (int i = 0; i < topk; ++i)
-        if (slot_c[i] >= 0) acc = fmaf(ds_slot[i], load_f(lk_head + (int64_t)slot_c[i] * dl + d), acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i >= topk) break;
+        // empty slots have ds_slot = 0; chunk 0 stands in so every load is issued
+        const int c = slot_c[i] >= 0 ? slot_c[i] : 0;
+        acc = fmaf(ds_slot[i], load_f(lk_head + (int64_t)c * dl + d), acc);
+      }
       dlq_row[d] = score_scale * acc;
     }
   }
@@ -163,32 +172,49 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
 
 // ---------------------------------------------------------------------------
 // bf16 query-side backward (S = D = 64).  Two waves; wave w owns rows 32w..
+// The next valid slot's K and V tiles stream into the other half of a
+// double-buffered swizzled LDS area while the current slot is computed.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_bwd_q_bf16(
+__global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
     const bf16* __restrict__ dout, const bf16* __restrict__ lk, bf16* __restrict__ dq,
     float* __restrict__ dw_out, float* __restrict__ dscore_out, float* __restrict__ dlq,
     float* __restrict__ delta, int64_t n_query, int64_t n_key, int topk, int dl,
     float attn_scale, float score_scale) {
-  __shared__ bf16 k_lds[64 * kLdsStrideB];
-  __shared__ bf16 v_lds[64 * kLdsStrideB];
+  __shared__ __align__(16) bf16 k_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 v_lds[2][kTileElems];
   __shared__ float dw_part[2][16];
   __shared__ int slot_c[16];
   __shared__ float slot_w[16];
   __shared__ float dw_slot[16];
   __shared__ float ds_slot[16];
+  __shared__ int s_list[16];
+  __shared__ int s_n;
+  __shared__ int s_mask;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int64_t head = tile / n_query;
   const int x = 32 * wave + col;
 
-  if (tid < topk) {
-    const int c = idx[tile * topk + tid];
-    slot_c[tid] = (c >= 0 && c < n_key) ? c : -1;
-    slot_w[tid] = w[tile * topk + tid];
+  if (wave == 0) {  // slot table and compact list of the valid slots, in one step
+    const int i = lane < topk ? lane : 0;
+    const int c = idx[tile * topk + i];
+    const float wv = w[tile * topk + i];
+    const bool ok = lane < topk && c >= 0 && c < n_key;
+    const uint64_t mask = __ballot(ok);
+    if (lane < topk) {
+      slot_c[lane] = ok ? c : -1;
+      slot_w[lane] = wv;
+    }
+    if (ok) s_list[__popcll(mask & ((1ull << lane) - 1))] = lane;
+    if (lane == 0) {
+      s_n = __popcll(mask);
+      s_mask = (int)mask;
+    }
   }
+  if (tid < 32) dw_part[tid >> 4][tid & 15] = 0.0f;
   bf16x8 bq[4], bdo[4];
   {
     const bf16* qr = q + tile * 4096 + x * 64 + 32 * half;
@@ -202,20 +228,32 @@ __global__ __launch_bounds__(128) void k_bwd_q_bf16(
   f32x16 dqacc[2] = {zero16(), zero16()};
   const float c2 = attn_scale * kLog2e;
   __syncthreads();
-
-  for (int i = 0; i < topk; ++i) {
-    const int c = slot_c[i];
-    float* drow = delta + (tile * topk + i) * 64;
-    if (c < 0) {
-      if (half == 0) drow[x] = 0.0f;
-      if (lane == 0) dw_part[wave][i] = 0.0f;
-      continue;
-    }
+  const int n = s_n;
+  if (half == 0)
+    for (int i = 0; i < topk; ++i)
+      if (!((s_mask >> i) & 1)) delta[(tile * topk + i) * 64 + x] = 0.0f;
+  float l2_next = 0.0f;
+  if (n > 0) {
+    const int i0 = s_list[0];
+    tile_dma<2>(k_lds[0], kk + (head * n_key + slot_c[i0]) * 4096, wave, lane);
+    tile_dma<2>(v_lds[0], v + (head * n_key + slot_c[i0]) * 4096, wave, lane);
+    l2_next = lse[(tile * topk + i0) * 64 + x] * kLog2e;
+  }
+  for (int u = 0; u < n; ++u) {
+    const int buf = u & 1;
+    const int i = s_list[u];
     const float wi = slot_w[i];
+    wait_vmem();
     __syncthreads();
-    tile64_to_lds<128>(k_lds, kk + (head * n_key + c) * 4096, tid);
-    tile64_to_lds<128>(v_lds, v + (head * n_key + c) * 4096, tid);
-    __syncthreads();
+    const float l2 = l2_next;
+    if (u + 1 < n) {
+      const int i1 = s_list[u + 1];
+      tile_dma<2>(k_lds[buf ^ 1], kk + (head * n_key + slot_c[i1]) * 4096, wave, lane);
+      tile_dma<2>(v_lds[buf ^ 1], v + (head * n_key + slot_c[i1]) * 4096, wave, lane);
+      l2_next = lse[(tile * topk + i1) * 64 + x] * kLog2e;
+    }
+    const bf16* kt = k_lds[buf];
+    const bf16* vt = v_lds[buf];
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -223,12 +261,10 @@ __global__ __launch_bounds__(128) void k_bwd_q_bf16(
       pacc[mt] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int off = (32 * mt + col) * kLdsStrideB + 32 * half + 8 * ks;
-        sacc[mt] = mfma32x32x16(*(const bf16x8*)(k_lds + off), bq[ks], sacc[mt]);
-        pacc[mt] = mfma32x32x16(*(const bf16x8*)(v_lds + off), bdo[ks], pacc[mt]);
+        sacc[mt] = mfma32x32x16(lds_row8(kt, 32 * mt + col, 4 * half + ks), bq[ks], sacc[mt]);
+        pacc[mt] = mfma32x32x16(lds_row8(vt, 32 * mt + col, 4 * half + ks), bdo[ks], pacc[mt]);
       }
     }
-    const float l2 = lse[(tile * topk + i) * 64 + x] * kLog2e;
     float dsum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -239,7 +275,7 @@ __global__ __launch_bounds__(128) void k_bwd_q_bf16(
         dsum = fmaf(p, pacc[mt][r], dsum);
       }
     dsum += __shfl_xor(dsum, 32);
-    if (half == 0) drow[x] = dsum;
+    if (half == 0) delta[(tile * topk + i) * 64 + x] = dsum;
     const float part = wave_sum(half == 0 ? dsum : 0.0f);
     if (lane == 0) dw_part[wave][i] = part;
     // dS^T = w P (dP~ - D), then dQ^T (d x x) += K^T (d x j) dS^T (j x x)
@@ -254,16 +290,8 @@ __global__ __launch_bounds__(128) void k_bwd_q_bf16(
       }
       const int j0 = 16 * ks + 4 * half;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x8 ak;
-        const bf16* kc = k_lds + 32 * dt + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ak[e] = kc[(j0 + e) * kLdsStrideB];
-          ak[4 + e] = kc[(j0 + 8 + e) * kLdsStrideB];
-        }
-        dqacc[dt] = mfma32x32x16(ak, bs, dqacc[dt]);
-      }
+      for (int dt = 0; dt < 2; ++dt)
+        dqacc[dt] = mfma32x32x16(lds_tr_operand(kt, 32 * dt, j0, j0 + 8, lane), bs, dqacc[dt]);
     }
   }
   bf16* dqrow = dq + tile * 4096 + x * 64;
@@ -286,8 +314,13 @@ __global__ __launch_bounds__(128) void k_bwd_q_bf16(
 
 // ---------------------------------------------------------------------------
 // bf16 key-side backward (S = D = 64).  Two waves; wave w owns key rows 32w..
+// The reverse-list entries are staged in LDS 128 at a time; the next entry's
+// Q and dO tiles stream into the other half of a double-buffered swizzled LDS
+// area and its log-sum-exp / D rows and scalars into registers while the
+// current entry is computed.  The 64 query rows of a pair are processed in two
+// halves of 32 so that only half of S and dP~ is live at a time.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_bwd_kv_bf16(
+__global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
@@ -295,10 +328,11 @@ __global__ __launch_bounds__(128) void k_bwd_kv_bf16(
     const float* __restrict__ dscore, bf16* __restrict__ dk, bf16* __restrict__ dv,
     float* __restrict__ dlk, int64_t n_query, int64_t n_key, int topk, int dl,
     float attn_scale, float score_scale) {
-  __shared__ bf16 q_lds[64 * kLdsStrideB];
-  __shared__ bf16 do_lds[64 * kLdsStrideB];
-  __shared__ float l2_lds[64];
-  __shared__ float d_lds[64];
+  __shared__ __align__(16) bf16 q_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 do_lds[2][kTileElems];
+  __shared__ __align__(16) float l2_lds[2][64];
+  __shared__ __align__(16) float d_lds[2][64];
+  __shared__ int s_ent[128];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_key + c
@@ -323,72 +357,85 @@ __global__ __launch_bounds__(128) void k_bwd_kv_bf16(
   const int beg = rev_off[head * (n_key + 1) + c];
   const int end = rev_off[head * (n_key + 1) + c + 1];
   const int32_t* ents = rev_ent + head * n_query * topk;
+  const int64_t pair0 = head * n_query * topk;
 
-  for (int e = beg; e < end; ++e) {
-    const int ent = ents[e];
-    const int64_t t = ent / topk;
-    const int64_t pair = head * n_query * topk + ent;  // (head, t, i)
-    const float wi = w[pair];
+  for (int b0 = beg; b0 < end; b0 += 128) {
+    const int nb = (end - b0) < 128 ? (end - b0) : 128;
+    __syncthreads();  // every wave is done with the previous block
+    if (tid < nb) s_ent[tid] = ents[b0 + tid];
     __syncthreads();
-    tile64_to_lds<128>(q_lds, q + (head * n_query + t) * 4096, tid);
-    tile64_to_lds<128>(do_lds, dout + (head * n_query + t) * 4096, tid);
-    if (tid < 64) {
-      l2_lds[tid] = lse[pair * 64 + tid] * kLog2e;
-      d_lds[tid] = delta[pair * 64 + tid];
-    }
-    if (lq && tid < dl)
-      dlk_acc = fmaf(dscore[pair], (float)lq[(head * n_query + t) * dl + tid], dlk_acc);
-    __syncthreads();
-    // S (x x j) = Q K_c^T and dP~ (x x j) = dO V_c^T; lane holds column j.
-    f32x16 sacc[2], pacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = zero16();
-      pacc[mt] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int off = (32 * mt + col) * kLdsStrideB + 32 * half + 8 * ks;
-        sacc[mt] = mfma32x32x16(*(const bf16x8*)(q_lds + off), bk[ks], sacc[mt]);
-        pacc[mt] = mfma32x32x16(*(const bf16x8*)(do_lds + off), bv[ks], pacc[mt]);
+    float rrow = 0.0f, rw = 0.0f, rds = 0.0f, rlq = 0.0f;
+    auto fetch = [&](int u, int buf) {
+      const int ent = s_ent[u];
+      const int64_t t = ent / topk;
+      const int64_t pair = pair0 + ent;
+      tile_dma<2>(q_lds[buf], q + (head * n_query + t) * 4096, wave, lane);
+      tile_dma<2>(do_lds[buf], dout + (head * n_query + t) * 4096, wave, lane);
+      rrow = tid < 64 ? lse[pair * 64 + tid] * kLog2e : delta[pair * 64 + (tid - 64)];
+      rw = w[pair];
+      if (lq) {
+        rds = dscore[pair];
+        rlq = tid < dl ? (float)lq[(head * n_query + t) * dl + tid] : 0.0f;
       }
-    }
-    // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
+    };
+    fetch(0, 0);
+    for (int u = 0; u < nb; ++u) {
+      const int buf = u & 1;
+      wait_vmem();
+      if (tid < 64)
+        l2_lds[buf][tid] = rrow;
+      else
+        d_lds[buf][tid - 64] = rrow;
+      const float wi = rw;
+      dlk_acc = fmaf(rds, rlq, dlk_acc);
+      __syncthreads();
+      if (u + 1 < nb) fetch(u + 1, buf ^ 1);
+      const bf16* qt = q_lds[buf];
+      const bf16* dot = do_lds[buf];
+      const float* l2r = l2_lds[buf];
+      const float* dr = d_lds[buf];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query rows 32mt .. 32mt+31
+        f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int xr = 32 * mt + c_row(r, half);
-        const float pw = wi * fast_exp2(fmaf(sacc[mt][r], c2, -l2_lds[xr]));
-        sacc[mt][r] = pw;
-        pacc[mt][r] = pw * (pacc[mt][r] - d_lds[xr]);
-      }
-    // dV^T (d x j) += dO^T (d x x) P_w (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, g0 = 2 * (ks & 1);
-      bf16x8 bp, bs;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bp[e] = (bf16)sacc[mt][4 * g0 + e];
-        bp[4 + e] = (bf16)sacc[mt][4 * g0 + 4 + e];
-        bs[e] = (bf16)pacc[mt][4 * g0 + e];
-        bs[4 + e] = (bf16)pacc[mt][4 * g0 + 4 + e];
-      }
-      const int x0 = 16 * ks + 4 * half;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x8 ado, aq;
-        const bf16* dc = do_lds + 32 * dt + col;
-        const bf16* qc = q_lds + 32 * dt + col;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ado[u] = dc[(x0 + u) * kLdsStrideB];
-          ado[4 + u] = dc[(x0 + 8 + u) * kLdsStrideB];
-          aq[u] = qc[(x0 + u) * kLdsStrideB];
-          aq[4 + u] = qc[(x0 + 8 + u) * kLdsStrideB];
+        for (int ks = 0; ks < 4; ++ks) {
+          sacc = mfma32x32x16(lds_row8(qt, 32 * mt + col, 4 * half + ks), bk[ks], sacc);
+          pacc = mfma32x32x16(lds_row8(dot, 32 * mt + col, 4 * half + ks), bv[ks], pacc);
         }
-        dvacc[dt] = mfma32x32x16(ado, bp, dvacc[dt]);
-        dkacc[dt] = mfma32x32x16(aq, bs, dkacc[dt]);
+        // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int x0 = 32 * mt + 8 * g + 4 * half;
+          const f32x4 l4 = *(const f32x4*)(l2r + x0);
+          const f32x4 d4 = *(const f32x4*)(dr + x0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float pw = wi * fast_exp2(fmaf(sacc[r], c2, -l4[e]));
+            sacc[r] = pw;
+            pacc[r] = pw * (pacc[r] - d4[e]);
+          }
+        }
+        // dV^T (d x j) += dO^T (d x x) P_w (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const int g0 = 2 * kk2;
+          bf16x8 bp, bs;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bp[e] = (bf16)sacc[4 * g0 + e];
+            bp[4 + e] = (bf16)sacc[4 * g0 + 4 + e];
+            bs[e] = (bf16)pacc[4 * g0 + e];
+            bs[4 + e] = (bf16)pacc[4 * g0 + 4 + e];
+          }
+          const int x0 = 32 * mt + 16 * kk2 + 4 * half;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            dvacc[dt] = mfma32x32x16(lds_tr_operand(dot, 32 * dt, x0, x0 + 8, lane), bp, dvacc[dt]);
+            dkacc[dt] = mfma32x32x16(lds_tr_operand(qt, 32 * dt, x0, x0 + 8, lane), bs, dkacc[dt]);
+          }
+        }
       }
     }
   }
@@ -581,39 +628,50 @@ __global__ __launch_bounds__(64) void k_bwd_kv_f32(
 hipError_t launch_backward(const LaunchBackward& a) {
   const int64_t heads = a.G * a.B * a.H;
   if (heads == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_reverse_index, dim3((unsigned)heads), dim3(256), 0, a.stream, a.idx,
+  {
+  KernelTimer timer(kKernReverseIndex, a.stream);
+  hipLaunchKernelGGL(k_reverse_index, dim3((unsigned)heads), dim3(512), 0, a.stream, a.idx,
                      a.n_query, a.n_key, a.k, a.rev_off, a.rev_ent);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
   if (a.dtype == 1) {
-    if (qtiles > 0)
+    if (qtiles > 0) {
+      KernelTimer timer(kKernBackwardQ, a.stream);
       hipLaunchKernelGGL(k_bwd_q_bf16, dim3((unsigned)qtiles), dim3(128), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                          a.lse, (const bf16*)a.dout, (const bf16*)a.lk, (bf16*)a.dq, a.dw,
                          a.dscore, a.dlq, a.delta, a.n_query, a.n_key, a.k, a.dl,
                          a.attn_scale, a.score_scale);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ktiles > 0)
+    if (ktiles > 0) {
+      KernelTimer timer(kKernBackwardKV, a.stream);
       hipLaunchKernelGGL(k_bwd_kv_bf16, dim3((unsigned)ktiles), dim3(128), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.w, a.lse,
                          (const bf16*)a.dout, a.delta, a.rev_off, a.rev_ent, (const bf16*)a.lq,
                          a.dscore, (bf16*)a.dk, (bf16*)a.dv, a.dlk, a.n_query, a.n_key, a.k,
                          a.dl, a.attn_scale, a.score_scale);
+    }
   } else {
-    if (qtiles > 0)
+    if (qtiles > 0) {
+      KernelTimer timer(kKernBackwardQ, a.stream);
       hipLaunchKernelGGL(k_bwd_q_f32, dim3((unsigned)qtiles), dim3(64), 0, a.stream,
                          (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.idx, a.w,
                          a.lse, (const float*)a.dout, (const float*)a.lk, (float*)a.dq, a.dw,
                          a.dscore, a.dlq, a.delta, a.n_query, a.n_key, a.S, a.D, a.k, a.dl,
                          a.attn_scale, a.score_scale);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ktiles > 0)
+    if (ktiles > 0) {
+      KernelTimer timer(kKernBackwardKV, a.stream);
       hipLaunchKernelGGL(k_bwd_kv_f32, dim3((unsigned)ktiles), dim3(64), 0, a.stream,
                          (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.w, a.lse,
                          (const float*)a.dout, a.delta, a.rev_off, a.rev_ent,
                          (const float*)a.lq, a.dscore, (float*)a.dk, (float*)a.dv, a.dlk,
                          a.n_query, a.n_key, a.S, a.D, a.k, a.dl, a.attn_scale, a.score_scale);
+    }
   }
   return hipGetLastError();
 }

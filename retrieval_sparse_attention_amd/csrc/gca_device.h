@@ -101,6 +101,67 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// LDS tiles: 64 rows x 64 bf16 with 128-byte rows, XOR-swizzled at 16-byte
+// granularity: chunk c (columns 8c .. 8c+7) of row r sits at chunk position
+// c ^ (r & 7).  Eight consecutive rows reading the same logical chunk, and the
+// 4-row x 16-column blocks of the transpose read, then hit distinct banks.
+constexpr int kTileElems = 64 * 64;
+
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous copy of one 64 x 64 bf16 tile (row-major, 128 B rows) from
+// global memory straight into a swizzled LDS tile with gfx950's 16-byte
+// global_load_lds: NW waves each move 8/NW pieces of 1 KB (8 rows).  The data
+// is in LDS once the issuing wave's vector-memory counter drains
+// (wait_vmem()) and a barrier has passed.
+template <int NW>
+__device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* __restrict__ src, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int r = 0; r < 8 / NW; ++r) {
+    const int piece = wave * (8 / NW) + r;
+    const int row = piece * 8 + (lane >> 3), pc = lane & 7;
+    __builtin_amdgcn_global_load_lds((const void*)(src + row * 64 + ((pc ^ (row & 7)) << 3)),
+                                     (lds_void*)(lds_tile + piece * 512), 16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16-byte read of row `row`, logical chunk `chunk` of a swizzled tile.
+__device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int row, int chunk) {
+  return *(const bf16x8*)(tile + swz(row, 8 * chunk));
+}
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, if lane s points at row r0 + s/4, columns c0 + 4*(s%4) .. +3 of a
+// 16-bit tile, lane i receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// MFMA operand whose lane owns column (c_base + lane % 32) of a swizzled LDS
+// tile and whose 8 contraction values are the tile rows r_a .. r_a+3 and
+// r_b .. r_b+3 (the caller picks r_a, r_b per lane half).  Two transpose
+// reads replace eight 2-byte reads.
+__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int c_base, int r_a, int r_b,
+                                                 int lane) {
+  const int s = lane & 15;
+  const int col = c_base + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const bf16x4 a = lds_read_tr(tile + swz(r_a + (s >> 2), col));
+  const bf16x4 b = lds_read_tr(tile + swz(r_b + (s >> 2), col));
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 __device__ __forceinline__ float load_f(const float* p) { return *p; }
 __device__ __forceinline__ float load_f(const bf16* p) { return (float)(*p); }
 

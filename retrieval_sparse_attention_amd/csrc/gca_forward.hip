@@ -7,7 +7,10 @@
 //
 // bf16 path (S = D = 64).  One workgroup of two waves per query chunk; wave w
 // owns query rows 32w .. 32w+31.  Per retrieved chunk:
-//   1. the K and V tiles (8 KB each) are copied into LDS with 16-byte loads;
+//   1. the K and V tiles (8 KB each) of the next retrieved chunk stream from
+//      global memory straight into the other half of a double-buffered,
+//      XOR-swizzled LDS area (global_load_lds) while the current chunk is
+//      computed; one barrier per chunk;
 //   2. S^T = K Q^T on MFMA (A = K rows from LDS, B = Q^T kept in registers), so a
 //      lane holds 32 of the 64 logits of ONE query row and the partner lane
 //      (l ^ 32) the other 32: the row max and row sum need one exchange;
@@ -15,8 +18,9 @@
 //      L = attn_scale * max + ln l;
 //   4. the fusion weight is folded into the probabilities, p * (w_i / l), which
 //      become the B operand of O^T += V^T P^T directly from the S^T registers,
-//      so all k slots accumulate into ONE float32 accumulator.  Each chunk's
-//      softmax is complete inside one 64-key tile: no running rescale is needed.
+//      so all k slots accumulate into ONE float32 accumulator; V^T comes from
+//      LDS through the gfx950 transpose read.  Each chunk's softmax is
+//      complete inside one 64-key tile: no running rescale is needed.
 // O is rounded to bf16 once at the end.
 //
 // f32 path.  One thread per query row, float32 throughout (small workloads).
@@ -26,31 +30,41 @@
 
 namespace gca {
 
-constexpr int kLdsStride = 72;  // bf16 per LDS tile row: 64 + 8 pad (conflict-free b128 reads)
-
-// Copies one 64 x 64 bf16 tile (row-major, 128 B rows) into LDS with 16-byte
-// loads; `nthreads` threads cooperate.
-template <int NTHREADS>
-__device__ __forceinline__ void tile_to_lds(bf16* dst, const bf16* __restrict__ src, int tid) {
-#pragma unroll
-  for (int r = 0; r < 512 / NTHREADS; ++r) {
-    const int ch = tid + NTHREADS * r;
-    const int row = ch >> 3, c8 = (ch & 7) * 8;
-    *(bf16x8*)(dst + row * kLdsStride + c8) = *(const bf16x8*)(src + row * 64 + c8);
-  }
-}
-
 __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ o,
     float* __restrict__ lse, int64_t n_query, int64_t n_key, int topk, float attn_scale) {
-  __shared__ bf16 k_lds[64 * kLdsStride];
-  __shared__ bf16 v_lds[64 * kLdsStride];
+  __shared__ __align__(16) bf16 k_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 v_lds[2][kTileElems];
+  __shared__ int s_c[16];
+  __shared__ float s_w[16];
+  __shared__ int s_slot[16];
+  __shared__ int s_n;
+  __shared__ int s_mask;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
   const int64_t head = tile / n_query;
   const int x = 32 * wave + col;  // query row owned by this lane
+
+  // compact list of the valid slots, built in one step from a wave ballot
+  if (wave == 0) {
+    const int i = lane < topk ? lane : 0;
+    const int c = idx[tile * topk + i];
+    const float wv = w[tile * topk + i];
+    const bool ok = lane < topk && c >= 0 && c < n_key;
+    const uint64_t mask = __ballot(ok);
+    if (ok) {
+      const int pos = __popcll(mask & ((1ull << lane) - 1));
+      s_c[pos] = c;
+      s_w[pos] = wv;
+      s_slot[pos] = lane;
+    }
+    if (lane == 0) {
+      s_n = __popcll(mask);
+      s_mask = (int)mask;
+    }
+  }
 
   bf16x8 bq[4];  // Q^T as the B operand: column x, dims 32*half + 8*ks + 0..7
   {
@@ -60,37 +74,36 @@ __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
   }
   f32x16 oacc[2] = {zero16(), zero16()};
   const float c2 = attn_scale * kLog2e;
-
-  for (int i = 0; i < topk; ++i) {
-    const int c = idx[tile * topk + i];
-    const float wi = w[tile * topk + i];
-    float* lse_row = lse ? lse + (tile * topk + i) * 64 : nullptr;
-    if (c < 0 || c >= n_key) {
-      if (lse_row && half == 0) lse_row[x] = -__builtin_huge_valf();
-      continue;
+  __syncthreads();
+  const int n = s_n;
+  if (lse && half == 0)  // empty slots read lse = -inf
+    for (int i = 0; i < topk; ++i)
+      if (!((s_mask >> i) & 1)) lse[(tile * topk + i) * 64 + x] = -__builtin_huge_valf();
+  if (n > 0) {
+    tile_dma<2>(k_lds[0], kk + (head * n_key + s_c[0]) * 4096, wave, lane);
+    tile_dma<2>(v_lds[0], v + (head * n_key + s_c[0]) * 4096, wave, lane);
+  }
+  for (int u = 0; u < n; ++u) {
+    const int buf = u & 1;
+    wait_vmem();
+    __syncthreads();  // tiles of slot u are in LDS; slot u-1 is done with the other buffer
+    if (u + 1 < n) {
+      tile_dma<2>(k_lds[buf ^ 1], kk + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
+      tile_dma<2>(v_lds[buf ^ 1], v + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
     }
-    const bf16* kt = kk + (head * n_key + c) * 4096;
-    const bf16* vt = v + (head * n_key + c) * 4096;
-    __syncthreads();  // the previous slot is done with the LDS tiles
-    tile_to_lds<128>(k_lds, kt, tid);
-    tile_to_lds<128>(v_lds, vt, tid);
-    __syncthreads();
-
+    const bf16* kt = k_lds[buf];
+    const bf16* vt = v_lds[buf];
     f32x16 sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       sacc[mt] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(k_lds + (32 * mt + col) * kLdsStride + 32 * half + 8 * ks);
-        sacc[mt] = mfma32x32x16(a, bq[ks], sacc[mt]);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[mt] = mfma32x32x16(lds_row8(kt, 32 * mt + col, 4 * half + ks), bq[ks], sacc[mt]);
     }
-    float m = sacc[0][0];
+    float m = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[mt][r]);
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(sacc[0][r], sacc[1][r]));
     m = fmaxf(m, __shfl_xor(m, 32));
     const float mb = m * c2;
     float l = 0.0f;
@@ -103,13 +116,13 @@ __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
         l += e;
       }
     l += __shfl_xor(l, 32);
-    if (lse_row && half == 0) lse_row[x] = attn_scale * m + logf(l);
-    const float ps = wi / l;
+    if (lse && half == 0) lse[(tile * topk + s_slot[u]) * 64 + x] = attn_scale * m + logf(l);
+    const float ps = s_w[u] / l;
 
     // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step ks covers keys
     // 16ks + 4*half + 0..3 and 16ks + 8 + 4*half + 0..3, which are exactly the
     // rows of S^T this lane holds in registers 4*g .. 4*g+3 for g = 2(ks&1),
-    // 2(ks&1)+1 of key tile ks/2.
+    // 2(ks&1)+1 of key tile ks/2; V^T comes from LDS by transpose reads.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int mt = ks >> 1, g0 = 2 * (ks & 1);
@@ -121,16 +134,8 @@ __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
       }
       const int j0 = 16 * ks + 4 * half;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        bf16x8 av;
-        const bf16* vc = v_lds + 32 * dt + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          av[e] = vc[(j0 + e) * kLdsStride];
-          av[4 + e] = vc[(j0 + 8 + e) * kLdsStride];
-        }
-        oacc[dt] = mfma32x32x16(av, bp, oacc[dt]);
-      }
+      for (int dt = 0; dt < 2; ++dt)
+        oacc[dt] = mfma32x32x16(lds_tr_operand(vt, 32 * dt, j0, j0 + 8, lane), bp, oacc[dt]);
     }
   }
   // O[x][d]: this lane holds d = 32dt + 8g + 4*half + 0..3 for its row x.
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(
 hipError_t launch_forward(const LaunchForward& a) {
   const int64_t tiles = a.G * a.B * a.H * a.n_query;
   if (tiles == 0) return hipSuccess;
+  KernelTimer timer(kKernForward, a.stream);
   if (a.dtype == 1) {
     hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(128), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,

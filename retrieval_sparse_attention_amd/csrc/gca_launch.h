@@ -71,6 +71,32 @@ struct LaunchBackward {
   hipStream_t stream;
 };
 
+// Kernels the library launches, for the event timing facility.
+enum KernelId {
+  kKernScan = 0,
+  kKernMerge = 1,
+  kKernForward = 2,
+  kKernReverseIndex = 3,
+  kKernBackwardQ = 4,
+  kKernBackwardKV = 5,
+  kNumKernels = 6
+};
+
+// Records a HIP event pair around one kernel launch on `stream` when timing is
+// enabled (gca_timing_enable); otherwise does nothing.
+class KernelTimer {
+ public:
+  KernelTimer(int kernel_id, hipStream_t stream);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  int kid_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
 hipError_t launch_retrieve(const ScanPlan& plan, const LaunchRetrieve& a);
 hipError_t launch_forward(const LaunchForward& a);
 hipError_t launch_backward(const LaunchBackward& a);

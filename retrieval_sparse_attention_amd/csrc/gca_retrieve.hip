@@ -149,14 +149,23 @@ __global__ __launch_bounds__(256) void k_scan_topk_bf16(
   int id[KMAX];
   list_clear(s, id);
 
+  // Each wave walks blocks of 32 candidates (stride 128); the next block's
+  // landmarks are loaded while the current block is scored.  Rows past n_key
+  // are read from the last row (in bounds) and masked out by j < n_cand.
   const bf16* lk_head = lk + head * n_key * DL + HALF * half;
-  for (int64_t blk = c_begin + 32 * wave; blk < c_end; blk += 128) {
-    const int64_t row = blk + col;
-    const bool row_ok = row < n_key;
-    bf16x8 a[NKS];
+  auto load_block = [&](int64_t blk, bf16x8 (&a)[NKS]) {
+    int64_t row = blk + col;
+    row = row < n_key ? row : n_key - 1;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      a[ks] = row_ok ? *(const bf16x8*)(lk_head + row * DL + 8 * ks) : zero_bf16x8();
+    for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const bf16x8*)(lk_head + row * DL + 8 * ks);
+  };
+  bf16x8 a[NKS];
+  int64_t blk = c_begin + 32 * wave;
+  if (blk < c_end) load_block(blk, a);
+  for (; blk < c_end; blk += 128) {
+    bf16x8 an[NKS];
+    const bool more = blk + 128 < c_end;
+    if (more) load_block(blk + 128, an);
     f32x16 acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) acc = mfma32x32x16(a[ks], bq[ks], acc);
@@ -166,6 +175,10 @@ __global__ __launch_bounds__(256) void k_scan_topk_bf16(
       const float x = acc[r] * score_scale;
       const bool hit = (j < c_end) && (j < n_cand) && better(x, (int)j, s[KMAX - 1], id[KMAX - 1]);
       if (hit) list_insert(s, id, x, (int)j);
+    }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) a[ks] = an[ks];
     }
   }
 
@@ -294,6 +307,8 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
   const int64_t heads = a.G * a.B * a.H;
   if (a.dtype == 1) {
     const int64_t nblk = heads * pl.nsplit * pl.n_qtiles;
+    {
+    KernelTimer timer(kKernScan, a.stream);
     if (a.dl == 64)
       hipLaunchKernelGGL((k_scan_topk_bf16<64, KMAX>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
@@ -304,15 +319,18 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,
                          a.softmax_one, a.idx, a.score, a.w, a.part_s, a.part_i);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t rows = heads * a.n_query;
+    KernelTimer timer(kKernMerge, a.stream);
     hipLaunchKernelGGL((k_topk_merge<KMAX>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                        a.stream, a.part_s, a.part_i, rows, pl.nsplit, a.k, a.softmax_one, a.idx,
                        a.score, a.w);
     return hipGetLastError();
   }
   const int64_t rows = heads * a.n_query;
+  KernelTimer timer(kKernScan, a.stream);
   hipLaunchKernelGGL((k_scan_topk_f32<KMAX>), dim3((unsigned)((rows + 63) / 64)), dim3(64), 0,
                      a.stream, (const float*)a.lq, (const float*)a.lk, a.q_pos, heads,
                      a.n_query, a.n_key, a.dl, a.score_scale, a.k, a.softmax_one, a.idx,

@@ -203,7 +203,7 @@ def kv_tiles_host(t, chunks):
     return out
 
 
-def query_batch(name, lk, step=0, seed=None, accept=None, **override):
+def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, **override):
     """Query chunks of a long-context workload with one planted needle each.
 
     For query chunk n the needle is resident chunk needle[n] (distinct per
@@ -211,6 +211,7 @@ def query_batch(name, lk, step=0, seed=None, accept=None, **override):
       lq = |g| (0.9 u + sqrt(1 - 0.81) v)
     with u the unit needle landmark, v a random unit vector orthogonal to u and
     |g| the norm of a fresh N(0, value_scale^2) draw, rounded to the stored dtype.
+    `accept_heads` (list of (g, b, h)) limits the redraw rule to those heads.
     Returns dict q [G,B,H,Nq,S,D], lq [G,B,H,Nq,Dl], q_pos [Nq], needle [Nq].
     """
     cfg = workload(name, **override)
@@ -245,6 +246,8 @@ def query_batch(name, lk, step=0, seed=None, accept=None, **override):
         for g in range(G):
             for b in range(B):
                 for h in range(H):
+                    if accept_heads is not None and (g, b, h) not in accept_heads:
+                        continue
                     todo = np.arange(Nq)
                     while todo.size:
                         ok = accept(_f64(lq[g, b, h, todo]), lk64[g, b, h, :n_cand],
