@@ -171,11 +171,12 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
 }
 
 // ---------------------------------------------------------------------------
-// bf16 query-side backward (S = D = 64).  Two waves; wave w owns rows 32w..
-// The next valid slot's K and V tiles stream into the other half of a
-// double-buffered swizzled LDS area while the current slot is computed.
+// bf16 query-side backward (S = D = 64).  Four waves; wave w owns query rows
+// 16w .. 16w+15 on 16x16x32 MFMA tiles.  The next valid slot's K and V tiles
+// stream into the other half of a double-buffered swizzled LDS area while the
+// current slot is computed.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
+__global__ __launch_bounds__(256) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
     const bf16* __restrict__ dout, const bf16* __restrict__ lk, bf16* __restrict__ dq,
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
     float attn_scale, float score_scale) {
   __shared__ __align__(16) bf16 k_lds[2][kTileElems];
   __shared__ __align__(16) bf16 v_lds[2][kTileElems];
-  __shared__ float dw_part[2][16];
+  __shared__ float dw_part[4][16];
   __shared__ int slot_c[16];
   __shared__ float slot_w[16];
   __shared__ float dw_slot[16];
@@ -193,10 +194,10 @@ __global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
   __shared__ int s_n;
   __shared__ int s_mask;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int64_t head = tile / n_query;
-  const int x = 32 * wave + col;
+  const int x = 16 * wave + col;
 
   if (wave == 0) {  // slot table and compact list of the valid slots, in one step
     const int i = lane < topk ? lane : 0;
@@ -214,29 +215,29 @@ __global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
       s_mask = (int)mask;
     }
   }
-  if (tid < 32) dw_part[tid >> 4][tid & 15] = 0.0f;
-  bf16x8 bq[4], bdo[4];
+  if (tid < 64) dw_part[tid >> 4][tid & 15] = 0.0f;
+  bf16x8 bq[2], bdo[2];  // Q^T and dO^T as B operands: column x, dims 32kd + 8grp + 0..7
   {
-    const bf16* qr = q + tile * 4096 + x * 64 + 32 * half;
-    const bf16* dr = dout + tile * 4096 + x * 64 + 32 * half;
+    const bf16* qr = q + tile * 4096 + x * 64 + 8 * grp;
+    const bf16* dr = dout + tile * 4096 + x * 64 + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bq[ks] = *(const bf16x8*)(qr + 8 * ks);
-      bdo[ks] = *(const bf16x8*)(dr + 8 * ks);
+    for (int kd = 0; kd < 2; ++kd) {
+      bq[kd] = *(const bf16x8*)(qr + 32 * kd);
+      bdo[kd] = *(const bf16x8*)(dr + 32 * kd);
     }
   }
-  f32x16 dqacc[2] = {zero16(), zero16()};
+  f32x4 dqacc[4] = {zero4(), zero4(), zero4(), zero4()};
   const float c2 = attn_scale * kLog2e;
   __syncthreads();
   const int n = s_n;
-  if (half == 0)
+  if (grp == 0)
     for (int i = 0; i < topk; ++i)
       if (!((s_mask >> i) & 1)) delta[(tile * topk + i) * 64 + x] = 0.0f;
   float l2_next = 0.0f;
   if (n > 0) {
     const int i0 = s_list[0];
-    tile_dma<2>(k_lds[0], kk + (head * n_key + slot_c[i0]) * 4096, wave, lane);
-    tile_dma<2>(v_lds[0], v + (head * n_key + slot_c[i0]) * 4096, wave, lane);
+    tile_dma<4>(k_lds[0], kk + (head * n_key + slot_c[i0]) * 4096, wave, lane);
+    tile_dma<4>(v_lds[0], v + (head * n_key + slot_c[i0]) * 4096, wave, lane);
     l2_next = lse[(tile * topk + i0) * 64 + x] * kLog2e;
   }
   for (int u = 0; u < n; ++u) {
@@ -248,79 +249,78 @@ __global__ __launch_bounds__(128, 2) void k_bwd_q_bf16(
     const float l2 = l2_next;
     if (u + 1 < n) {
       const int i1 = s_list[u + 1];
-      tile_dma<2>(k_lds[buf ^ 1], kk + (head * n_key + slot_c[i1]) * 4096, wave, lane);
-      tile_dma<2>(v_lds[buf ^ 1], v + (head * n_key + slot_c[i1]) * 4096, wave, lane);
+      tile_dma<4>(k_lds[buf ^ 1], kk + (head * n_key + slot_c[i1]) * 4096, wave, lane);
+      tile_dma<4>(v_lds[buf ^ 1], v + (head * n_key + slot_c[i1]) * 4096, wave, lane);
       l2_next = lse[(tile * topk + i1) * 64 + x] * kLog2e;
     }
     const bf16* kt = k_lds[buf];
     const bf16* vt = v_lds[buf];
-    f32x16 sacc[2], pacc[2];
+    // S^T = K Q^T and dP~^T = V dO^T per key tile mt; lane holds keys 16mt + 4grp + r.
+    f32x4 sacc[4], pacc[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = zero16();
-      pacc[mt] = zero16();
+    for (int mt = 0; mt < 4; ++mt) {
+      sacc[mt] = zero4();
+      pacc[mt] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        sacc[mt] = mfma32x32x16(lds_row8(kt, 32 * mt + col, 4 * half + ks), bq[ks], sacc[mt]);
-        pacc[mt] = mfma32x32x16(lds_row8(vt, 32 * mt + col, 4 * half + ks), bdo[ks], pacc[mt]);
+      for (int kd = 0; kd < 2; ++kd) {
+        sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
+        pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
       }
     }
     float dsum = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(fmaf(sacc[mt][r], c2, -l2));
         sacc[mt][r] = p;
         dsum = fmaf(p, pacc[mt][r], dsum);
       }
+    dsum += __shfl_xor(dsum, 16);
     dsum += __shfl_xor(dsum, 32);
-    if (half == 0) delta[(tile * topk + i) * 64 + x] = dsum;
-    const float part = wave_sum(half == 0 ? dsum : 0.0f);
+    if (grp == 0) delta[(tile * topk + i) * 64 + x] = dsum;
+    const float part = wave_sum(grp == 0 ? dsum : 0.0f);
     if (lane == 0) dw_part[wave][i] = part;
-    // dS^T = w P (dP~ - D), then dQ^T (d x x) += K^T (d x j) dS^T (j x x)
+    // dS^T = w P (dP~ - D); dQ^T (d x x) += K^T (d x j) dS^T (j x x)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, g0 = 2 * (ks & 1);
+    for (int kb = 0; kb < 2; ++kb) {
       bf16x8 bs;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bs[e] = (bf16)(wi * sacc[mt][4 * g0 + e] * (pacc[mt][4 * g0 + e] - dsum));
-        bs[4 + e] = (bf16)(wi * sacc[mt][4 * g0 + 4 + e] * (pacc[mt][4 * g0 + 4 + e] - dsum));
+        bs[e] = (bf16)(wi * sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
+        bs[4 + e] = (bf16)(wi * sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
       }
-      const int j0 = 16 * ks + 4 * half;
+      const int j0 = 32 * kb + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        dqacc[dt] = mfma32x32x16(lds_tr_operand(kt, 32 * dt, j0, j0 + 8, lane), bs, dqacc[dt]);
+      for (int dt = 0; dt < 4; ++dt)
+        dqacc[dt] = mfma16x16x32(lds_tr_operand16(kt, 16 * dt, j0, j0 + 16, lane), bs, dqacc[dt]);
     }
   }
-  bf16* dqrow = dq + tile * 4096 + x * 64;
+  bf16* dqrow = dq + tile * 4096 + x * 64 + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 4; ++dt) {
+    bf16x4 val;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 val;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (bf16)(attn_scale * dqacc[dt][4 * g + e]);
-      *(bf16x4*)(dqrow + 32 * dt + 8 * g + 4 * half) = val;
-    }
+    for (int e = 0; e < 4; ++e) val[e] = (bf16)(attn_scale * dqacc[dt][e]);
+    *(bf16x4*)(dqrow + 16 * dt) = val;
+  }
   __syncthreads();
-  if (tid < topk) dw_slot[tid] = dw_part[0][tid] + dw_part[1][tid];
+  if (tid < topk) dw_slot[tid] = (dw_part[0][tid] + dw_part[1][tid]) + (dw_part[2][tid] + dw_part[3][tid]);
   __syncthreads();
-  score_epilogue<bf16>(tid, 128, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
+  score_epilogue<bf16>(tid, 256, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
                        dscore_out + tile * topk, lk ? lk + head * n_key * dl : nullptr,
                        dlq ? dlq + tile * dl : nullptr, dl, score_scale);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 key-side backward (S = D = 64).  Two waves; wave w owns key rows 32w..
-// The reverse-list entries are staged in LDS 128 at a time; the next entry's
-// Q and dO tiles stream into the other half of a double-buffered swizzled LDS
-// area and its log-sum-exp / D rows and scalars into registers while the
-// current entry is computed.  The 64 query rows of a pair are processed in two
-// halves of 32 so that only half of S and dP~ is live at a time.
+// bf16 key-side backward (S = D = 64).  Four waves; wave w owns key rows
+// 16w .. 16w+15 on 16x16x32 MFMA tiles.  The reverse-list entries are staged
+// in LDS 128 at a time; the next entry's Q and dO tiles stream into the other
+// half of a double-buffered swizzled LDS area and its log-sum-exp / D rows and
+// scalars into registers while the current entry is computed.  The 64 query
+// rows of a pair are processed as two 32-row contraction steps.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
+__global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
@@ -332,26 +332,26 @@ __global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
   __shared__ __align__(16) bf16 do_lds[2][kTileElems];
   __shared__ __align__(16) float l2_lds[2][64];
   __shared__ __align__(16) float d_lds[2][64];
-  __shared__ int s_ent[128];
+  __shared__ int s_ent[256];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_key + c
   const int64_t head = tile / n_key;
   const int64_t c = tile % n_key;
-  const int j = 32 * wave + col;  // key row owned by this lane
+  const int j = 16 * wave + col;  // key row owned by this lane
 
-  bf16x8 bk[4], bv[4];  // K_c^T and V_c^T as B operands: column j
+  bf16x8 bk[2], bv[2];  // K_c^T and V_c^T as B operands: column j, dims 32kd + 8grp + 0..7
   {
-    const bf16* kr = kk + tile * 4096 + j * 64 + 32 * half;
-    const bf16* vr = v + tile * 4096 + j * 64 + 32 * half;
+    const bf16* kr = kk + tile * 4096 + j * 64 + 8 * grp;
+    const bf16* vr = v + tile * 4096 + j * 64 + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bk[ks] = *(const bf16x8*)(kr + 8 * ks);
-      bv[ks] = *(const bf16x8*)(vr + 8 * ks);
+    for (int kd = 0; kd < 2; ++kd) {
+      bk[kd] = *(const bf16x8*)(kr + 32 * kd);
+      bv[kd] = *(const bf16x8*)(vr + 32 * kd);
     }
   }
-  f32x16 dkacc[2] = {zero16(), zero16()};
-  f32x16 dvacc[2] = {zero16(), zero16()};
+  f32x4 dkacc[4] = {zero4(), zero4(), zero4(), zero4()};
+  f32x4 dvacc[4] = {zero4(), zero4(), zero4(), zero4()};
   float dlk_acc = 0.0f;
   const float c2 = attn_scale * kLog2e;
   const int beg = rev_off[head * (n_key + 1) + c];
@@ -359,8 +359,8 @@ __global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
   const int32_t* ents = rev_ent + head * n_query * topk;
   const int64_t pair0 = head * n_query * topk;
 
-  for (int b0 = beg; b0 < end; b0 += 128) {
-    const int nb = (end - b0) < 128 ? (end - b0) : 128;
+  for (int b0 = beg; b0 < end; b0 += 256) {
+    const int nb = (end - b0) < 256 ? (end - b0) : 256;
     __syncthreads();  // every wave is done with the previous block
     if (tid < nb) s_ent[tid] = ents[b0 + tid];
     __syncthreads();
@@ -369,9 +369,10 @@ __global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
       const int ent = s_ent[u];
       const int64_t t = ent / topk;
       const int64_t pair = pair0 + ent;
-      tile_dma<2>(q_lds[buf], q + (head * n_query + t) * 4096, wave, lane);
-      tile_dma<2>(do_lds[buf], dout + (head * n_query + t) * 4096, wave, lane);
-      rrow = tid < 64 ? lse[pair * 64 + tid] * kLog2e : delta[pair * 64 + (tid - 64)];
+      tile_dma<4>(q_lds[buf], q + (head * n_query + t) * 4096, wave, lane);
+      tile_dma<4>(do_lds[buf], dout + (head * n_query + t) * 4096, wave, lane);
+      if (tid < 128)
+        rrow = tid < 64 ? lse[pair * 64 + tid] * kLog2e : delta[pair * 64 + (tid - 64)];
       rw = w[pair];
       if (lq) {
         rds = dscore[pair];
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
       wait_vmem();
       if (tid < 64)
         l2_lds[buf][tid] = rrow;
-      else
+      else if (tid < 128)
         d_lds[buf][tid - 64] = rrow;
       const float wi = rw;
       dlk_acc = fmaf(rds, rlq, dlk_acc);
@@ -395,65 +396,62 @@ __global__ __launch_bounds__(128, 2) void k_bwd_kv_bf16(
       const float* l2r = l2_lds[buf];
       const float* dr = d_lds[buf];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query rows 32mt .. 32mt+31
-        f32x16 sacc = zero16(), pacc = zero16();
+      for (int kb = 0; kb < 2; ++kb) {
+        // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query tiles 2kb, 2kb+1;
+        // the lane holds rows x = 32kb + 16h + 4grp + r of its key column j.
+        f32x4 sacc[2], pacc[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          sacc = mfma32x32x16(lds_row8(qt, 32 * mt + col, 4 * half + ks), bk[ks], sacc);
-          pacc = mfma32x32x16(lds_row8(dot, 32 * mt + col, 4 * half + ks), bv[ks], pacc);
-        }
-        // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
+        for (int h = 0; h < 2; ++h) {
+          const int xr = 32 * kb + 16 * h + col;
+          sacc[h] = zero4();
+          pacc[h] = zero4();
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int x0 = 32 * mt + 8 * g + 4 * half;
+          for (int kd = 0; kd < 2; ++kd) {
+            sacc[h] = mfma16x16x32(lds_row8(qt, xr, 4 * kd + grp), bk[kd], sacc[h]);
+            pacc[h] = mfma16x16x32(lds_row8(dot, xr, 4 * kd + grp), bv[kd], pacc[h]);
+          }
+          // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
+          const int x0 = 32 * kb + 16 * h + 4 * grp;
           const f32x4 l4 = *(const f32x4*)(l2r + x0);
           const f32x4 d4 = *(const f32x4*)(dr + x0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const float pw = wi * fast_exp2(fmaf(sacc[r], c2, -l4[e]));
-            sacc[r] = pw;
-            pacc[r] = pw * (pacc[r] - d4[e]);
+            const float pw = wi * fast_exp2(fmaf(sacc[h][e], c2, -l4[e]));
+            sacc[h][e] = pw;
+            pacc[h][e] = pw * (pacc[h][e] - d4[e]);
           }
         }
         // dV^T (d x j) += dO^T (d x x) P_w (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
+        bf16x8 bp, bs;
 #pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int g0 = 2 * kk2;
-          bf16x8 bp, bs;
+        for (int e = 0; e < 4; ++e) {
+          bp[e] = (bf16)sacc[0][e];
+          bp[4 + e] = (bf16)sacc[1][e];
+          bs[e] = (bf16)pacc[0][e];
+          bs[4 + e] = (bf16)pacc[1][e];
+        }
+        const int x0 = 32 * kb + 4 * grp;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bp[e] = (bf16)sacc[4 * g0 + e];
-            bp[4 + e] = (bf16)sacc[4 * g0 + 4 + e];
-            bs[e] = (bf16)pacc[4 * g0 + e];
-            bs[4 + e] = (bf16)pacc[4 * g0 + 4 + e];
-          }
-          const int x0 = 32 * mt + 16 * kk2 + 4 * half;
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            dvacc[dt] = mfma32x32x16(lds_tr_operand(dot, 32 * dt, x0, x0 + 8, lane), bp, dvacc[dt]);
-            dkacc[dt] = mfma32x32x16(lds_tr_operand(qt, 32 * dt, x0, x0 + 8, lane), bs, dkacc[dt]);
-          }
+        for (int dt = 0; dt < 4; ++dt) {
+          dvacc[dt] = mfma16x16x32(lds_tr_operand16(dot, 16 * dt, x0, x0 + 16, lane), bp, dvacc[dt]);
+          dkacc[dt] = mfma16x16x32(lds_tr_operand16(qt, 16 * dt, x0, x0 + 16, lane), bs, dkacc[dt]);
         }
       }
     }
   }
-  bf16* dkrow = dk + tile * 4096 + j * 64;
-  bf16* dvrow = dv + tile * 4096 + j * 64;
+  bf16* dkrow = dk + tile * 4096 + j * 64 + 4 * grp;
+  bf16* dvrow = dv + tile * 4096 + j * 64 + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 4; ++dt) {
+    bf16x4 kv4, vv4;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 kv4, vv4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv4[e] = (bf16)(attn_scale * dkacc[dt][4 * g + e]);
-        vv4[e] = (bf16)dvacc[dt][4 * g + e];
-      }
-      *(bf16x4*)(dkrow + 32 * dt + 8 * g + 4 * half) = kv4;
-      *(bf16x4*)(dvrow + 32 * dt + 8 * g + 4 * half) = vv4;
+    for (int e = 0; e < 4; ++e) {
+      kv4[e] = (bf16)(attn_scale * dkacc[dt][e]);
+      vv4[e] = (bf16)dvacc[dt][e];
     }
+    *(bf16x4*)(dkrow + 16 * dt) = kv4;
+    *(bf16x4*)(dvrow + 16 * dt) = vv4;
+  }
   if (dlk && tid < dl) dlk[tile * dl + tid] = score_scale * dlk_acc;
 }
 
@@ -639,7 +637,7 @@ hipError_t launch_backward(const LaunchBackward& a) {
   if (a.dtype == 1) {
     if (qtiles > 0) {
       KernelTimer timer(kKernBackwardQ, a.stream);
-      hipLaunchKernelGGL(k_bwd_q_bf16, dim3((unsigned)qtiles), dim3(128), 0, a.stream,
+      hipLaunchKernelGGL(k_bwd_q_bf16, dim3((unsigned)qtiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                          a.lse, (const bf16*)a.dout, (const bf16*)a.lk, (bf16*)a.dq, a.dw,
                          a.dscore, a.dlq, a.delta, a.n_query, a.n_key, a.k, a.dl,
@@ -648,7 +646,7 @@ hipError_t launch_backward(const LaunchBackward& a) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
-      hipLaunchKernelGGL(k_bwd_kv_bf16, dim3((unsigned)ktiles), dim3(128), 0, a.stream,
+      hipLaunchKernelGGL(k_bwd_kv_bf16, dim3((unsigned)ktiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.w, a.lse,
                          (const bf16*)a.dout, a.delta, a.rev_off, a.rev_ent, (const bf16*)a.lq,
                          a.dscore, (bf16*)a.dk, (bf16*)a.dv, a.dlk, a.n_query, a.n_key, a.k,

@@ -30,6 +30,26 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16 (wave64):
+//   A (16 x 32): lane l supplies row (l % 16), 8 K-values
+//   B (32 x 16): lane l supplies column (l % 16), 8 K-values
+//   C/D (16 x 16): lane l, register r holds C[4*(l/16) + r][l % 16]
+// The four 16-lane groups supply the four 8-wide quarters of the contraction.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// Larger of two values (the library is built without NaN semantics, so this is
+// a plain v_max_f32 / v_max3_f32).
+__device__ __forceinline__ float max_nc(float a, float b) { return fmaxf(a, b); }
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -161,6 +181,22 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int c_base, i
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
+
+// Operand for a 16x16x32 MFMA whose lane owns column (c_base + lane % 16) of a
+// swizzled LDS tile and whose 8 contraction values are the tile rows
+// r_a .. r_a+3 and r_b .. r_b+3 (picked per 16-lane group by the caller).
+__device__ __forceinline__ bf16x8 lds_tr_operand16(const bf16* tile, int c_base, int r_a, int r_b,
+                                                   int lane) {
+  const int s = lane & 15;
+  const int col = c_base + 4 * (s & 3);
+  const bf16x4 a = lds_read_tr(tile + swz(r_a + (s >> 2), col));
+  const bf16x4 b = lds_read_tr(tile + swz(r_b + (s >> 2), col));
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
 
 __device__ __forceinline__ float load_f(const float* p) { return *p; }
 __device__ __forceinline__ float load_f(const bf16* p) { return (float)(*p); }

@@ -5,15 +5,16 @@
 // separately to the S tokens of each retrieved chunk c_i, giving O^i[x] and the
 // log-sum-exp L_i[x]; the output is O[x] = sum_i w_i O^i[x].
 //
-// bf16 path (S = D = 64).  One workgroup of two waves per query chunk; wave w
-// owns query rows 32w .. 32w+31.  Per retrieved chunk:
+// bf16 path (S = D = 64).  One workgroup of four waves per query chunk; wave w
+// owns query rows 16w .. 16w+15 and works on 16x16x32 MFMA tiles.  Per
+// retrieved chunk:
 //   1. the K and V tiles (8 KB each) of the next retrieved chunk stream from
 //      global memory straight into the other half of a double-buffered,
 //      XOR-swizzled LDS area (global_load_lds) while the current chunk is
 //      computed; one barrier per chunk;
 //   2. S^T = K Q^T on MFMA (A = K rows from LDS, B = Q^T kept in registers), so a
-//      lane holds 32 of the 64 logits of ONE query row and the partner lane
-//      (l ^ 32) the other 32: the row max and row sum need one exchange;
+//      lane holds 16 of the 64 logits of ONE query row and the lanes l ^ 16,
+//      l ^ 32, l ^ 48 the others: the row max and row sum need two exchanges;
 //   3. p = exp2((s - max) * attn_scale * log2 e), l = sum p,
 //      L = attn_scale * max + ln l;
 //   4. the fusion weight is folded into the probabilities, p * (w_i / l), which
@@ -30,7 +31,7 @@
 
 namespace gca {
 
-__global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
+__global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ o,
     float* __restrict__ lse, int64_t n_query, int64_t n_key, int topk, float attn_scale) {
@@ -42,10 +43,10 @@ __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
   __shared__ int s_n;
   __shared__ int s_mask;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
   const int64_t head = tile / n_query;
-  const int x = 32 * wave + col;  // query row owned by this lane
+  const int x = 16 * wave + col;  // query row owned by this lane
 
   // compact list of the valid slots, built in one step from a wave ballot
   if (wave == 0) {
@@ -65,90 +66,90 @@ __global__ __launch_bounds__(128) void k_fwd_bf16_s64d64(
       s_mask = (int)mask;
     }
   }
-
-  bf16x8 bq[4];  // Q^T as the B operand: column x, dims 32*half + 8*ks + 0..7
+  bf16x8 bq[2];  // Q^T as the B operand: column x, dims 32*kd + 8*grp + 0..7
   {
-    const bf16* row = q + tile * 4096 + x * 64 + 32 * half;
+    const bf16* row = q + tile * 4096 + x * 64 + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bq[ks] = *(const bf16x8*)(row + 8 * ks);
+    for (int kd = 0; kd < 2; ++kd) bq[kd] = *(const bf16x8*)(row + 32 * kd);
   }
-  f32x16 oacc[2] = {zero16(), zero16()};
+  f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
   const float c2 = attn_scale * kLog2e;
   __syncthreads();
   const int n = s_n;
-  if (lse && half == 0)  // empty slots read lse = -inf
+  if (lse && grp == 0)  // empty slots read lse = -inf
     for (int i = 0; i < topk; ++i)
       if (!((s_mask >> i) & 1)) lse[(tile * topk + i) * 64 + x] = -__builtin_huge_valf();
   if (n > 0) {
-    tile_dma<2>(k_lds[0], kk + (head * n_key + s_c[0]) * 4096, wave, lane);
-    tile_dma<2>(v_lds[0], v + (head * n_key + s_c[0]) * 4096, wave, lane);
+    tile_dma<4>(k_lds[0], kk + (head * n_key + s_c[0]) * 4096, wave, lane);
+    tile_dma<4>(v_lds[0], v + (head * n_key + s_c[0]) * 4096, wave, lane);
   }
   for (int u = 0; u < n; ++u) {
     const int buf = u & 1;
     wait_vmem();
     __syncthreads();  // tiles of slot u are in LDS; slot u-1 is done with the other buffer
     if (u + 1 < n) {
-      tile_dma<2>(k_lds[buf ^ 1], kk + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
-      tile_dma<2>(v_lds[buf ^ 1], v + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
+      tile_dma<4>(k_lds[buf ^ 1], kk + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
+      tile_dma<4>(v_lds[buf ^ 1], v + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
     }
     const bf16* kt = k_lds[buf];
     const bf16* vt = v_lds[buf];
-    f32x16 sacc[2];
+    // S^T = K Q^T: key tile mt (16 keys) x this wave's 16 queries; the lane
+    // holds keys 16mt + 4*grp + r of its query column x.
+    f32x4 sacc[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = zero16();
+    for (int mt = 0; mt < 4; ++mt) {
+      sacc[mt] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc[mt] = mfma32x32x16(lds_row8(kt, 32 * mt + col, 4 * half + ks), bq[ks], sacc[mt]);
+      for (int kd = 0; kd < 2; ++kd)
+        sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
     }
-    float m = fmaxf(sacc[0][0], sacc[1][0]);
+    float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
 #pragma unroll
-    for (int r = 1; r < 16; ++r) m = fmaxf(m, fmaxf(sacc[0][r], sacc[1][r]));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    for (int r = 1; r < 4; ++r)
+      m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
+    m = max_nc(m, __shfl_xor(m, 16));
+    m = max_nc(m, __shfl_xor(m, 32));
     const float mb = m * c2;
     float l = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const float e = fast_exp2(fmaf(sacc[mt][r], c2, -mb));
         sacc[mt][r] = e;
         l += e;
       }
+    l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (lse && half == 0) lse[(tile * topk + s_slot[u]) * 64 + x] = attn_scale * m + logf(l);
+    if (lse && grp == 0) lse[(tile * topk + s_slot[u]) * 64 + x] = attn_scale * m + logf(l);
     const float ps = s_w[u] / l;
 
-    // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step ks covers keys
-    // 16ks + 4*half + 0..3 and 16ks + 8 + 4*half + 0..3, which are exactly the
-    // rows of S^T this lane holds in registers 4*g .. 4*g+3 for g = 2(ks&1),
-    // 2(ks&1)+1 of key tile ks/2; V^T comes from LDS by transpose reads.
+    // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step kb covers keys
+    // 32kb + 4*grp + 0..3 (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile
+    // 2kb+1): exactly what this lane holds; V^T comes by transpose reads.
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mt = ks >> 1, g0 = 2 * (ks & 1);
+    for (int kb = 0; kb < 2; ++kb) {
       bf16x8 bp;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bp[e] = (bf16)(sacc[mt][4 * g0 + e] * ps);
-        bp[4 + e] = (bf16)(sacc[mt][4 * g0 + 4 + e] * ps);
+        bp[e] = (bf16)(sacc[2 * kb][e] * ps);
+        bp[4 + e] = (bf16)(sacc[2 * kb + 1][e] * ps);
       }
-      const int j0 = 16 * ks + 4 * half;
+      const int j0 = 32 * kb + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        oacc[dt] = mfma32x32x16(lds_tr_operand(vt, 32 * dt, j0, j0 + 8, lane), bp, oacc[dt]);
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = mfma16x16x32(lds_tr_operand16(vt, 16 * dt, j0, j0 + 16, lane), bp, oacc[dt]);
     }
   }
-  // O[x][d]: this lane holds d = 32dt + 8g + 4*half + 0..3 for its row x.
-  bf16* orow = o + tile * 4096 + x * 64;
+  // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
+  bf16* orow = o + tile * 4096 + x * 64 + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 4; ++dt) {
+    bf16x4 val;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 val;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (bf16)oacc[dt][4 * g + e];
-      *(bf16x4*)(orow + 32 * dt + 8 * g + 4 * half) = val;
-    }
+    for (int e = 0; e < 4; ++e) val[e] = (bf16)oacc[dt][e];
+    *(bf16x4*)(orow + 16 * dt) = val;
+  }
 }
 
 // float32 path: 64 threads per query chunk, thread x owns query row x (< S).
@@ -214,7 +215,7 @@ hipError_t launch_forward(const LaunchForward& a) {
   if (tiles == 0) return hipSuccess;
   KernelTimer timer(kKernForward, a.stream);
   if (a.dtype == 1) {
-    hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(128), 0, a.stream,
+    hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(256), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                        (bf16*)a.o, a.lse, a.n_query, a.n_key, a.k, a.attn_scale);
   } else {
