@@ -267,6 +267,14 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
         pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
       }
     }
+    // K^T operands of this slot, requested now so that the LDS latency overlaps
+    // the elementwise arithmetic below.
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
     float dsum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -276,10 +284,9 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
         sacc[mt][r] = p;
         dsum = fmaf(p, pacc[mt][r], dsum);
       }
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
+    dsum = xor32_sum(xor16_sum(dsum));
     if (grp == 0) delta[(tile * topk + i) * 64 + x] = dsum;
-    const float part = wave_sum(grp == 0 ? dsum : 0.0f);
+    const float part = row16_sum(dsum);  // the 16 query rows of this wave
     if (lane == 0) dw_part[wave][i] = part;
     // dS^T = w P (dP~ - D); dQ^T (d x x) += K^T (d x j) dS^T (j x x)
 #pragma unroll
@@ -290,10 +297,8 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
         bs[e] = (bf16)(wi * sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
         bs[4 + e] = (bf16)(wi * sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
       }
-      const int j0 = 32 * kb + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        dqacc[dt] = mfma16x16x32(lds_tr_operand16(kt, 16 * dt, j0, j0 + 16, lane), bs, dqacc[dt]);
+      for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
     }
   }
   bf16* dqrow = dq + tile * 4096 + x * 64 + 4 * grp;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
 // scalars into registers while the current entry is computed.  The 64 query
 // rows of a pair are processed as two 32-row contraction steps.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
+__global__ __launch_bounds__(256) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
@@ -397,6 +402,14 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
       const float* dr = d_lds[buf];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // dO^T and Q^T operands of this contraction step, requested first so
+        // that their LDS latency overlaps the products and arithmetic below.
+        bf16x8 ado[4], aq[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          ado[dt] = lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+          aq[dt] = lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+        }
         // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query tiles 2kb, 2kb+1;
         // the lane holds rows x = 32kb + 16h + 4grp + r of its key column j.
         f32x4 sacc[2], pacc[2];
@@ -430,11 +443,10 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
           bs[e] = (bf16)pacc[0][e];
           bs[4 + e] = (bf16)pacc[1][e];
         }
-        const int x0 = 32 * kb + 4 * grp;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          dvacc[dt] = mfma16x16x32(lds_tr_operand16(dot, 16 * dt, x0, x0 + 16, lane), bp, dvacc[dt]);
-          dkacc[dt] = mfma16x16x32(lds_tr_operand16(qt, 16 * dt, x0, x0 + 16, lane), bs, dkacc[dt]);
+          dvacc[dt] = mfma16x16x32(ado[dt], bp, dvacc[dt]);
+          dkacc[dt] = mfma16x16x32(aq[dt], bs, dkacc[dt]);
         }
       }
     }

@@ -114,6 +114,45 @@ __device__ __forceinline__ void list_clear(float (&s)[KMAX], int (&id)[KMAX]) {
   }
 }
 
+// Cross-lane all-reduce steps on VALU lane swaps (gfx950), no LDS round trip.
+// permlane16_swap(x, x) returns, for every 16-lane row pair (0,1) and (2,3),
+// the first row's and the second row's values; permlane32_swap(x, x) returns
+// the two 32-lane halves.  op(r[0], r[1]) is therefore op(x[l], x[l ^ 16]) (or
+// l ^ 32), identical on both partners, for any commutative op.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over each 16-lane row, left in every lane of the row (DPP row rotates).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);  // row_ror:8
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x122>(v);  // row_ror:2
+  v += dpp_f<0x121>(v);  // row_ror:1
+  return v;
+}
+
 // Deterministic butterfly sum over the 64 lanes of a wave (every lane gets it).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

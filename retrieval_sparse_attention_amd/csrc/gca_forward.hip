@@ -103,12 +103,19 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
       for (int kd = 0; kd < 2; ++kd)
         sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
     }
+    // V^T operands of this slot, requested now so that the LDS latency overlaps
+    // the softmax arithmetic below.
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        va[kb][dt] = lds_tr_operand16(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
     float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
 #pragma unroll
     for (int r = 1; r < 4; ++r)
       m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
-    m = max_nc(m, __shfl_xor(m, 16));
-    m = max_nc(m, __shfl_xor(m, 32));
+    m = xor32_max(xor16_max(m));
     const float mb = m * c2;
     float l = 0.0f;
 #pragma unroll
@@ -119,8 +126,7 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
         sacc[mt][r] = e;
         l += e;
       }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = xor32_sum(xor16_sum(l));
     if (lse && grp == 0) lse[(tile * topk + s_slot[u]) * 64 + x] = attn_scale * m + logf(l);
     const float ps = s_w[u] / l;
 
@@ -135,10 +141,8 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
         bp[e] = (bf16)(sacc[2 * kb][e] * ps);
         bp[4 + e] = (bf16)(sacc[2 * kb + 1][e] * ps);
       }
-      const int j0 = 32 * kb + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = mfma16x16x32(lds_tr_operand16(vt, 16 * dt, j0, j0 + 16, lane), bp, oacc[dt]);
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma16x16x32(va[kb][dt], bp, oacc[dt]);
     }
   }
   // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
