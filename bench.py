@@ -35,8 +35,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-heads", type=int, default=12,
+    ap.add_argument("--cpu-heads", type=int, default=96,
                     help="(g, b, h) heads of one step the oracle runs for the CPU baseline")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 16M-token retrieval and 1M-token inference measurements")
+    ap.add_argument("--infer-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, one device-to-device copy of BYTES "
@@ -136,6 +139,135 @@ def cpu_baseline(x, cfg, n_heads):
                        f"{dt:.1f} s, scaled by {total_heads}/{len(heads)}")
 
 
+def _timed(fn, reps):
+    """Average ms of fn() over reps calls, on the current stream, plus per-kernel sums."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    gca.gca_timing_enable(True)
+    gca.gca_timing_collect()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    gca.gca_timing_enable(False)
+    per = {k: v[0] / v[1] for k, v in gca.gca_timing_collect().items() if v[1]}
+    return e0.elapsed_time(e1) / reps, per
+
+
+def bench_retrieve16m(reps=20):
+    """16,777,216-token resident context (262144 chunks of 64, K/V ~51.5 GB):
+    32 query chunks retrieve top-8 from every chunk, then attend and fuse."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+    name = "retrieve16m"
+    cfg = synth.workload(name)
+    lk = synth.context_landmarks(name)
+    qb = synth.query_batch(name, lk)
+    kd, vd = synth.device_kv(name, "cuda")
+    lkd, lqd, qd = lk.cuda(), qb["lq"].cuda(), qb["q"].cuda()
+    qpos = qb["q_pos"].cuda()
+    G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
+    shape = gca.make_shape(G, B, H, Nq, Nk, cfg["S"], cfg["D"], cfg["Dl"], cfg["k"], gca.GCA_BF16,
+                           cfg["softmax_one"])
+    k = cfg["k"]
+    idx = torch.empty((G, B, H, Nq, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((G, B, H, Nq, k), device="cuda")
+    w = torch.empty_like(score)
+    o = torch.empty_like(qd)
+    lse = torch.empty((G, B, H, Nq, k, cfg["S"]), device="cuda")
+    ws = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        gca.gca_retrieve(shape, lqd, lkd, qpos, idx, score, w, ws=ws)
+        gca.gca_forward(shape, qd, kd, vd, idx, w, o, lse)
+
+    for _ in range(3):
+        step()
+    ms, per = _timed(step, reps)
+    scan_ms = per.get("scan_topk", 0.0)
+    merge_ms = per.get("topk_merge", 0.0)
+    fwd_ms = per.get("forward", 0.0)
+    lk_bytes = G * B * H * Nk * cfg["Dl"] * 2
+    scores = G * B * H * Nq * Nk
+    best = torch.gather(idx, -1, score.argmax(-1, keepdim=True))[..., 0].cpu()
+    hits = float((best == qb["needle"].view(1, 1, 1, Nq)).float().mean())
+    del kd, vd
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens": Nk * cfg["S"], "query_chunks": Nq, "heads": H,
+            "retrieve_fwd_latency_ms": round(ms, 4),
+            "scan_us": round(scan_ms * 1e3, 2), "merge_us": round(merge_ms * 1e3, 2),
+            "forward_us": round(fwd_ms * 1e3, 2),
+            "landmark_scan_GBps": round(lk_bytes / (scan_ms * 1e-3) / 1e9, 1) if scan_ms else None,
+            "landmark_scan_roofline_frac": round(lk_bytes / (scan_ms * 1e-3) / HBM_PEAK, 4)
+            if scan_ms else None,
+            "topk_scores_per_s": round(scores / ((scan_ms + merge_ms) * 1e-3), 1)
+            if scan_ms else None,
+            "needle_hit_rate": hits, "reps": reps}
+
+
+def bench_infer1m(steps):
+    """1,048,576-token resident context (16384 chunks): per chunk step, one new
+    query chunk retrieves top-8 of 16383 candidates (with a planted needle),
+    attends and fuses.  Latency of each step from HIP events."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+    name = "infer1m_step"
+    cfg = synth.workload(name)
+    lk = synth.context_landmarks(name)
+    kd, vd = synth.device_kv(name, "cuda")
+    lkd = lk.cuda()
+    G, B, H, Nk, S, k = cfg["G"], cfg["B"], cfg["H"], cfg["n_key"], cfg["S"], cfg["k"]
+    lk64 = lk.to(torch.float64).numpy()
+    batches = [synth.query_batch(name, lk, step=s, lk64=lk64) for s in range(steps)]
+    qs = torch.stack([b["q"] for b in batches]).cuda()
+    lqs = torch.stack([b["lq"] for b in batches]).cuda()
+    needles = torch.stack([b["needle"] for b in batches])
+    qpos = batches[0]["q_pos"].cuda()
+    shape = gca.make_shape(G, B, H, 1, Nk, S, cfg["D"], cfg["Dl"], k, gca.GCA_BF16,
+                           cfg["softmax_one"])
+    idx = torch.empty((steps, G, B, H, 1, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((steps, G, B, H, 1, k), device="cuda")
+    w = torch.empty_like(score)
+    o = torch.empty_like(qs)
+    lse = torch.empty((steps, G, B, H, 1, k, S), device="cuda")
+    ws = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(s):
+        gca.gca_retrieve(shape, lqs[s], lkd, qpos, idx[s], score[s], w[s], ws=ws)
+        gca.gca_forward(shape, qs[s], kd, vd, idx[s], w[s], o[s], lse[s])
+
+    for s in range(10):
+        step(s)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for s in range(steps):
+        step(s)
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    lat = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]) * 1e3
+    best = torch.gather(idx, -1, score.argmax(-1, keepdim=True))[..., 0, 0].cpu()
+    hits = float((best == needles.view(steps, 1, 1, 1)).float().mean())
+    del kd, vd
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens": Nk * S, "steps": steps,
+            "step_latency_us_p50": round(float(np.percentile(lat, 50)), 2),
+            "step_latency_us_p99": round(float(np.percentile(lat, 99)), 2),
+            "step_latency_us_mean": round(float(lat.mean()), 2),
+            "needle_hit_rate": hits}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -229,6 +361,14 @@ def main():
         print(f"[bench] copy reference: {n} bytes read, {n} bytes written", file=sys.stderr,
               flush=True)
         del src, dst
+    long_ctx = {}
+    if not args.no_long_context:
+        long_ctx["retrieve16m"] = bench_retrieve16m()
+        print(f"[bench] 16M retrieval: {long_ctx['retrieve16m']['retrieve_fwd_latency_ms']} ms",
+              file=sys.stderr, flush=True)
+        long_ctx["infer1m_step"] = bench_infer1m(args.infer_steps)
+        print(f"[bench] 1M inference step p50: "
+              f"{long_ctx['infer1m_step']['step_latency_us_p50']} us", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, cfg, args.cpu_heads)
@@ -252,6 +392,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "long_context": long_ctx or None,
         "wall_s_timed": round(wall, 3),
         "source_digest": digest,
     }

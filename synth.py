@@ -203,7 +203,8 @@ def kv_tiles_host(t, chunks):
     return out
 
 
-def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, **override):
+def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, lk64=None,
+                **override):
     """Query chunks of a long-context workload with one planted needle each.
 
     For query chunk n the needle is resident chunk needle[n] (distinct per
@@ -212,6 +213,7 @@ def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, **o
     with u the unit needle landmark, v a random unit vector orthogonal to u and
     |g| the norm of a fresh N(0, value_scale^2) draw, rounded to the stored dtype.
     `accept_heads` (list of (g, b, h)) limits the redraw rule to those heads.
+    `lk64` may pass a float64 copy of lk (reused across many steps).
     Returns dict q [G,B,H,Nq,S,D], lq [G,B,H,Nq,Dl], q_pos [Nq], needle [Nq].
     """
     cfg = workload(name, **override)
@@ -224,7 +226,8 @@ def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, **o
     n_cand = max(0, min(q_pos_val - 1, Nk))
     needle = rs["needle"].choice(n_cand, size=Nq, replace=False)
     q = _normal(rs["q"], (G, B, H, Nq, S, D), sc, dt)
-    lk64 = _f64(lk)
+    if lk64 is None:
+        lk64 = _f64(lk)
 
     def draw(g, b, h, n, rng):
         u = lk64[g, b, h, needle[n]]
