@@ -104,6 +104,12 @@ gca_status check_shape(const gca_shape* s, int op, Sizes* z) {
   return GCA_OK;
 }
 
+#ifndef GCA_SCAN_TARGET_WGS
+#define GCA_SCAN_TARGET_WGS 768
+#endif
+constexpr int64_t kScanTargetWgs = GCA_SCAN_TARGET_WGS;
+constexpr int64_t kMergeMax = 4096;  // partial keys per query the merge kernel holds in LDS
+
 gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
   gca::ScanPlan p{};
   p.kmax = s->top_k <= 4 ? 4 : (s->top_k <= 8 ? 8 : 16);
@@ -115,10 +121,14 @@ gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
     if (p.split_len == 0) p.split_len = 128;
     return p;
   }
+  // Slice the candidates so that the grid has about kScanTargetWgs workgroups,
+  // with slices of whole 128-candidate rounds and at most kMergeMax partial
+  // entries per query for the merge.
   const int64_t base = z.heads * (p.n_qtiles > 0 ? p.n_qtiles : 1);
   const int64_t max_split = (s->n_key + 127) / 128;
-  int64_t want = (2048 + base - 1) / base;
+  int64_t want = (kScanTargetWgs + base - 1) / base;
   if (want > max_split) want = max_split;
+  if (want > kMergeMax / p.kmax) want = kMergeMax / p.kmax;
   if (want < 1) want = 1;
   int64_t len = (s->n_key + want - 1) / want;
   len = ((len + 127) / 128) * 128;
@@ -128,16 +138,15 @@ gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
 }
 
 struct RetrieveWs {
-  size_t part_s, part_i, total;
+  size_t part, total;
 };
 
 RetrieveWs retrieve_ws(const gca_shape* s, const Sizes& z, const gca::ScanPlan& p) {
-  RetrieveWs w{0, 0, 0};
+  RetrieveWs w{0, 0};
   if (p.nsplit <= 1) return w;
   const size_t n = (size_t)z.q_rows * (size_t)p.nsplit * (size_t)p.kmax;
-  w.part_s = 0;
-  w.part_i = align_up(n * sizeof(float));
-  w.total = w.part_i + align_up(n * sizeof(int32_t));
+  w.part = 0;
+  w.total = align_up(n * sizeof(uint64_t));
   (void)s;
   return w;
 }
@@ -254,8 +263,7 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
   a.idx = idx;
   a.score = score;
   a.w = w;
-  a.part_s = wl.total ? (float*)((char*)ws + wl.part_s) : nullptr;
-  a.part_i = wl.total ? (int32_t*)((char*)ws + wl.part_i) : nullptr;
+  a.part = wl.total ? (uint64_t*)((char*)ws + wl.part) : nullptr;
   a.stream = (hipStream_t)stream;
   return device_status(gca::launch_retrieve(plan, a), a.stream, "gca_retrieve");
 }

@@ -192,6 +192,11 @@ __device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* __restrict_
 // s_waitcnt vmcnt(0): every vector memory access of this wave has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt lgkmcnt(0): every LDS (and scalar memory) access of this wave has
+// completed.  Placed after a divergent LDS atomic, it settles the returned
+// value on every path, so later uses need no waits of their own.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // 16-byte read of row `row`, logical chunk `chunk` of a swizzled tile.
 __device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int row, int chunk) {
   return *(const bf16x8*)(tile + swz(row, 8 * chunk));

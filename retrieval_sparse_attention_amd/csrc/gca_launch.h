@@ -26,8 +26,7 @@ struct LaunchRetrieve {
   int32_t* idx;
   float* score;
   float* w;
-  float* part_s;    // [heads * n_query * nsplit * kmax] when nsplit > 1
-  int32_t* part_i;  // same
+  uint64_t* part;   // [heads * n_query * nsplit * kmax] candidate keys when nsplit > 1
   hipStream_t stream;
 };
 

@@ -7,16 +7,16 @@
 // authors' reply "Q4").
 //
 // bf16 path.  The scan is a dense contraction of 32 query landmarks with a
-// stream of candidate landmarks, so it runs on MFMA and stays bound by the
-// single pass over lk in HBM.  S^T = LK_block (32 x Dl) * LQ^T (Dl x 32) puts, in
-// each lane, 16 scores of ONE query; the lane keeps its own sorted top-KMAX list
-// in registers and only a score that beats the lane's current k-th best pays
-// for an insertion.  Each workgroup (4 waves) covers one 32-query tile and one
-// slice of candidates; its 8 lists per query are merged with a 3-level LDS
-// tree.  Large candidate sets are cut into slices that a second kernel merges.
+// stream of candidate landmarks, so it runs on MFMA and is bound by the single
+// pass over lk in HBM.  S^T = LK_block (32 x Dl) * LQ^T (Dl x 32) puts, in each
+// lane, 16 dot products of ONE query.  Selection is by threshold: only
+// candidates at or above a running lower bound of the k-th best score are
+// appended to a per-query LDS bucket, and the bucket is reduced to its exact
+// top k now and then (see k_scan_topk_bf16).  Large candidate sets are cut
+// into slices whose partial top-k lists a second kernel merges.
 //
-// f32 path.  One thread per query computes float32 dot products and the same
-// sorted list; it serves the small float32 workloads.
+// f32 path.  One thread per query computes float32 dot products and keeps a
+// sorted register list; it serves the small float32 workloads.
 
 #include "gca_device.h"
 #include "gca_launch.h"
@@ -81,37 +81,207 @@ __device__ void finalize_query(const float (&s_in)[KMAX], const int (&i_in)[KMAX
   }
 }
 
-// Merges two sorted lists held in LDS into the top KMAX of their union.
+// ---------------------------------------------------------------------------
+// Candidate keys.  A candidate (score x, chunk j) is packed into one 64-bit key
+// whose unsigned order is the selection order: the high word maps the float
+// bits of x to an order-preserving unsigned value, the low word is ~j, so that
+// among equal scores the lower chunk index is the larger key.  Key 0 is below
+// every real key and marks an empty entry.  Keys of one query are distinct
+// because chunk indices are.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ord_score(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t h = (uint32_t)(key >> 32);
+  return __uint_as_float((h & 0x80000000u) ? (h ^ 0x80000000u) : ~h);
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ uint64_t make_key(float x, int j) {
+  return ((uint64_t)ord_score(x) << 32) | (uint32_t)~(uint32_t)j;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Lower bound, in unscaled dot-product units, of every dot product a whose
+// score fl(a * scale) reaches t (inv_scale = 1 / scale, rounded): the relative
+// margin 2^-20 covers the three roundings involved and the absolute 1e-30
+// covers scores that underflow to zero.  -inf stays -inf.
+__device__ __forceinline__ float raw_bound(float t, float inv_scale) {
+  const float r = t * inv_scale;
+  return (r >= 0.0f ? r * (1.0f - 0x1p-20f) : r * (1.0f + 0x1p-20f)) - 1e-30f;
+}
+
+// Sorted (descending) key list -> the (score, index) list finalize_query takes.
 template <int KMAX>
-__device__ __forceinline__ void merge_lists(const float* as, const int* ai, const float* bs,
-                                            const int* bi, float (&os)[KMAX], int (&oi)[KMAX]) {
-  int pa = 0, pb = 0;
+__device__ __forceinline__ void keys_to_list(const uint64_t* keys, int m, float (&s)[KMAX],
+                                             int (&id)[KMAX]) {
 #pragma unroll
   for (int p = 0; p < KMAX; ++p) {
-    const float xa = as[pa], xb = bs[pb];
-    const int ja = ai[pa], jb = bi[pb];
-    const bool ta = better(xa, ja, xb, jb);
-    os[p] = ta ? xa : xb;
-    oi[p] = ta ? ja : jb;
-    pa += ta ? 1 : 0;
-    pb += ta ? 0 : 1;
+    const uint64_t key = keys[p];
+    s[p] = p < m ? key_score(key) : -__builtin_huge_valf();
+    id[p] = p < m ? key_index(key) : kIdxNone;
   }
 }
 
 // ---------------------------------------------------------------------------
 // bf16 scan.  Grid: heads * nsplit * n_qtiles workgroups of 256 threads.
+//
+// Each workgroup owns 32 queries and one slice of candidates, visited in
+// rounds of 128 (one 32-candidate block per wave).  Per query it keeps a
+// threshold tau (in unscaled dot-product units, see raw_bound), a sorted list
+// of the best keys found so far and an LDS bucket.  A candidate whose dot
+// product reaches tau is appended to its query's bucket; candidates below tau
+// cannot be in the top k.  Whenever a bucket could overflow in the next round,
+// and after the last round, the workgroup reduces list + bucket to the exact
+// top k and raises tau to the k-th best.  In the first round, where no tau
+// exists yet, each of the 8 groups of 16 candidates a query gets (4 waves x 2
+// lane halves) offers its c-th best (c = 1 for k <= 8, else 2) and the
+// smallest offer serves as tau: 8c >= k candidates reach it.  Exactness never
+// depends on tau's quality, only the amount of work does.
 // ---------------------------------------------------------------------------
+constexpr int kScanCap = 160;  // bucket entries per query (>= 128 + 16)
+// Row stride in 8-byte entries: room past kScanCap for the packed kept keys
+// and 2 spare slots, and odd, so the 32 rows a wave appends to at the same
+// position fall in 32 different bank pairs.
+constexpr int kScanStride = kScanCap + 25;
+#ifndef GCA_SCAN_PREFETCH
+#define GCA_SCAN_PREFETCH 2
+#endif
+constexpr int kScanPrefetch = GCA_SCAN_PREFETCH;  // landmark blocks in flight per wave
+
+// Bucket entries hold the raw dot product and the chunk index of a candidate;
+// the selection key (which needs the scaled score) is formed only here.
+struct ScanEntry {
+  float raw;
+  int j;
+};
+
+__device__ __forceinline__ uint64_t entry_key(ScanEntry e, float score_scale) {
+  return make_key(e.raw * score_scale + 0.0f, e.j);  // +0.0f: -0 scores compare as +0
+}
+
+// Exact top k of every query's kept list plus its bucket (256 threads: 8 per
+// query, all in one wave).  Afterwards kept[q] holds the sorted top-k keys,
+// the bucket is empty and tau_raw[q] bounds the k-th best from below.
+//  1. Thread `sub` of query q takes bucket entries sub, sub+8, ... and kept
+//     entries sub, sub+8, and finds its c-th best key (c = 1 for k <= 8, else
+//     2); the minimum over the 8 threads bounds the k-th best key from below
+//     (8c >= k distinct entries reach it).
+//  2. Keys at or above that bound are packed to the front of the bucket.
+//  3. Each packed key's rank is the number of packed keys above it; ranks
+//     below k give the sorted top k.
+// Kept out of line: the scan loop that calls it then has no inner loops, and
+// the compiler keeps precise load-wait counts across its iterations.
+template <int KMAX>
+__device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX],
+                                                       int* cnt, int* nkept, int* ncnt,
+                                                       float* tau_raw, int k, float score_scale,
+                                                       float inv_scale) {
+  constexpr int E = kScanCap / 8;
+  constexpr int EK = (KMAX + 7) / 8;
+  const int tid = threadIdx.x;
+  const int q = tid >> 3, sub = tid & 7;
+  ScanEntry* b = bucket + q * kScanStride;
+  const int n = cnt[q], nk = nkept[q];
+  // entries per thread this wave needs (its 8 queries' largest bucket)
+  int nw = n;
+  nw = max(nw, __shfl_xor(nw, 8));
+  nw = max(nw, __shfl_xor(nw, 16));
+  nw = max(nw, __shfl_xor(nw, 32));
+  const int per = (nw + 7) >> 3;
+  uint64_t e[E + EK];
+#pragma unroll
+  for (int p = 0; p < E; ++p) {
+    e[p] = 0;
+    if (p < per) {
+      const int i = sub + 8 * p;
+      const ScanEntry v = b[i];
+      e[p] = i < n ? entry_key(v, score_scale) : 0;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < EK; ++p) {
+    const int i = sub + 8 * p;
+    const uint64_t v = kept[q][i < KMAX ? i : 0];
+    e[E + p] = i < nk ? v : 0;
+  }
+  uint64_t m1 = 0, m2 = 0;
+#pragma unroll
+  for (int p = 0; p < E + EK; ++p) {
+    if (KMAX > 8) m2 = umax64(m2, umin64(m1, e[p]));
+    m1 = umax64(m1, e[p]);
+  }
+  uint64_t thr = (KMAX > 8 && k > 8) ? m2 : m1;
+  thr = umin64(thr, shfl_xor64(thr, 1));
+  thr = umin64(thr, shfl_xor64(thr, 2));
+  thr = umin64(thr, shfl_xor64(thr, 4));
+  if (sub == 0) ncnt[q] = 0;
+  __syncthreads();
+  uint64_t* pk = (uint64_t*)b;  // packed keys reuse the bucket row
+  int np = 0;
+#pragma unroll
+  for (int p = 0; p < E + EK; ++p) np += (e[p] != 0 && e[p] >= thr) ? 1 : 0;
+  int o = np ? atomicAdd(&ncnt[q], np) : 0;
+#pragma unroll
+  for (int p = 0; p < E + EK; ++p)
+    if (e[p] != 0 && e[p] >= thr) pk[o++] = e[p];
+  __syncthreads();
+  const int n2 = ncnt[q];
+  for (int u0 = 0; u0 < n2; u0 += 32) {
+    uint64_t mine[4];
+    int rank[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = u0 + sub + 8 * u;
+      mine[u] = i < n2 ? pk[i] : 0;
+      rank[u] = 0;
+    }
+    // f + 3 < n2 + 3 <= kScanCap + KMAX + 3 < kScanStride: reads stay in the row
+    for (int f = 0; f < n2; f += 4) {
+      uint64_t F[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) F[t] = f + t < n2 ? pk[f + t] : 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank[u] += F[t] > mine[u] ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (mine[u] != 0 && rank[u] < k) kept[q][rank[u]] = mine[u];
+  }
+  __syncthreads();
+  const int m = n2 < k ? n2 : k;
+  if (sub == 0) {
+    cnt[q] = 0;
+    nkept[q] = m;
+    tau_raw[q] = m == k ? raw_bound(key_score(kept[q][k - 1]), inv_scale) : -__builtin_huge_valf();
+  }
+  __syncthreads();
+}
+
 template <int DL, int KMAX>
-__global__ __launch_bounds__(256) void k_scan_topk_bf16(
+__global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
     const bf16* __restrict__ lq, const bf16* __restrict__ lk, const int32_t* __restrict__ q_pos,
     int64_t n_query, int64_t n_key, int n_qtiles, int nsplit, int64_t split_len,
     float score_scale, int k, int softmax_one, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, float* __restrict__ w_out, float* __restrict__ part_s,
-    int32_t* __restrict__ part_i) {
+    float* __restrict__ score_out, float* __restrict__ w_out, uint64_t* __restrict__ part) {
   constexpr int NKS = DL / 16;  // MFMA K-steps over the landmark dimension
   constexpr int HALF = DL / 2;  // landmark dims supplied by each lane half
-  __shared__ float ls[8][32][KMAX];
-  __shared__ int li[8][32][KMAX];
+  constexpr int PF = kScanPrefetch;
+  __shared__ ScanEntry bucket[32 * kScanStride];
+  __shared__ uint64_t kept[32][KMAX];  // sorted top keys of the compacted candidates
+  __shared__ int cnt[32], nkept[32], ncnt[32];
+  __shared__ float tau_raw[32];  // raw dot-product bound of the k-th best score
+  __shared__ uint32_t first_bound[32];  // min over groups of the ordered c-th best dot product
+  __shared__ int full[3];  // per round (mod 3): some bucket may overflow next round
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
@@ -129,13 +299,24 @@ __global__ __launch_bounds__(256) void k_scan_topk_bf16(
     n_cand = pos - 1 < n_key ? pos - 1 : n_key;
     if (n_cand < 0) n_cand = 0;
   }
-  // largest candidate count of the tile (all waves see the same 32 queries)
+  // largest candidate count of the tile (every wave sees the same 32 queries)
   int tile_max = (int)n_cand;  // n_key < 2^31 is checked on the host
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) tile_max = max(tile_max, __shfl_xor(tile_max, o));
+  tile_max = __builtin_amdgcn_readfirstlane(tile_max);  // uniform: keeps the loops scalar
   const int64_t c_begin = (int64_t)sp * split_len;
   int64_t c_end = c_begin + split_len;
   if (c_end > tile_max) c_end = tile_max;
+  const int64_t lim = n_cand < c_end ? n_cand : c_end;  // this lane's query: j < lim
+  const int c_first = (KMAX > 8 && k > 8) ? 2 : 1;
+
+  if (tid < 32) {
+    cnt[tid] = 0;
+    nkept[tid] = 0;
+    tau_raw[tid] = -__builtin_huge_valf();
+    first_bound[tid] = 0xFFFFFFFFu;
+  }
+  if (tid < 3) full[tid] = 0;
 
   bf16x8 bq[NKS];
   {
@@ -144,129 +325,216 @@ __global__ __launch_bounds__(256) void k_scan_topk_bf16(
     for (int ks = 0; ks < NKS; ++ks)
       bq[ks] = q_ok ? *(const bf16x8*)(row + 8 * ks) : zero_bf16x8();
   }
+  const float inv_scale = 1.0f / score_scale;
 
-  float s[KMAX];
-  int id[KMAX];
-  list_clear(s, id);
-
-  // Each wave walks blocks of 32 candidates (stride 128); the next block's
-  // landmarks are loaded while the current block is scored.  Rows past n_key
-  // are read from the last row (in bounds) and masked out by j < n_cand.
+  // Landmark rows: this lane reads row (block + col), half `half`, clamped to
+  // the last row: rows past the slice are read (in bounds) but never selected.
+  // Every round issues its loads unconditionally, so the compiler's wait
+  // counts let PF blocks per wave stay in flight.
   const bf16* lk_head = lk + head * n_key * DL + HALF * half;
   auto load_block = [&](int64_t blk, bf16x8 (&a)[NKS]) {
-    int64_t row = blk + col;
-    row = row < n_key ? row : n_key - 1;
+    const int64_t r = blk + col;
+    const bf16* p = lk_head + (r < n_key ? r : n_key - 1) * DL;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const bf16x8*)(lk_head + row * DL + 8 * ks);
+    for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const bf16x8*)(p + 8 * ks);
   };
-  bf16x8 a[NKS];
-  int64_t blk = c_begin + 32 * wave;
-  if (blk < c_end) load_block(blk, a);
-  for (; blk < c_end; blk += 128) {
-    bf16x8 an[NKS];
-    const bool more = blk + 128 < c_end;
-    if (more) load_block(blk + 128, an);
-    f32x16 acc = zero16();
+  const int n_rounds = c_end > c_begin ? (int)((c_end - c_begin + 127) >> 7) : 0;
+  bf16x8 ring[PF][NKS];  // slot s holds rounds s, s + PF, s + 2 PF, ...
+  if (n_rounds > 0) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) acc = mfma32x32x16(a[ks], bq[ks], acc);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t j = blk + c_row(r, half);
-      const float x = acc[r] * score_scale;
-      const bool hit = (j < c_end) && (j < n_cand) && better(x, (int)j, s[KMAX - 1], id[KMAX - 1]);
-      if (hit) list_insert(s, id, x, (int)j);
-    }
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) a[ks] = an[ks];
-    }
-  }
-
-  // 8 lists per query: g = 2 * wave + half.  Tree merge through LDS.
-  const int g = 2 * wave + half;
-#pragma unroll
-  for (int p = 0; p < KMAX; ++p) {
-    ls[g][col][p] = s[p];
-    li[g][col][p] = id[p];
+    for (int s = 0; s < PF; ++s) load_block(c_begin + 128 * s + 32 * wave, ring[s]);
   }
   __syncthreads();
+
+  // The overflow decision after round R reads full[R % 3], which only round R
+  // sets; it is cleared during round R + 2, after every wave has read it (two
+  // barriers later) and before round R + 3 can set it again.  Rounds past the
+  // slice (up to PF - 1 at the end) select nothing.
+  for (int round0 = 0; round0 < n_rounds; round0 += PF) {
 #pragma unroll
-  for (int step = 1; step < 8; step <<= 1) {
-    if ((g % (2 * step)) == 0) {
-      merge_lists<KMAX>(ls[g][col], li[g][col], ls[g + step][col], li[g + step][col], s, id);
+    for (int s = 0; s < PF; ++s) {
+      const int round = round0 + s;
+      const int64_t blk = c_begin + 128 * round + 32 * wave;
+      if (tid == 0) full[(round + 1) % 3] = 0;
+      f32x16 acc = zero16();
 #pragma unroll
-      for (int p = 0; p < KMAX; ++p) {
-        ls[g][col][p] = s[p];
-        li[g][col][p] = id[p];
+      for (int ks = 0; ks < NKS; ++ks) acc = mfma32x32x16(ring[s][ks], bq[ks], acc);
+      load_block(blk + 128 * PF, ring[s]);
+      // candidate blk + c_row(r, half) is eligible iff c_row(r, half) - 4*half < rem
+      const int64_t rem64 = lim - blk - 4 * half;
+      const int rem = rem64 < 0 ? 0 : (rem64 > 32 ? 32 : (int)rem64);
+      const bool whole = __all(rem >= 28);  // every row of the block is eligible
+      float tl = tau_raw[col];
+      if (round == 0) {
+        float m1 = -__builtin_huge_valf(), m2 = -__builtin_huge_valf();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float am = (8 * (r >> 2) + (r & 3)) < rem ? acc[r] : -__builtin_huge_valf();
+          if (KMAX > 8) m2 = fmaxf(m2, fminf(m1, am));
+          m1 = fmaxf(m1, am);
+        }
+        atomicMin(&first_bound[col], ord_score(c_first == 2 ? m2 : m1));
+        __syncthreads();
+        const uint32_t fb = first_bound[col];
+        const float b_raw = (fb & 0x80000000u) ? __uint_as_float(fb ^ 0x80000000u)
+                                               : __uint_as_float(~fb);
+        // the scores of the offered candidates reach fl(b_raw * scale); the
+        // bound stays valid for every later round
+        tl = fmaxf(tl, raw_bound(b_raw * score_scale + 0.0f, inv_scale));
+        if (tid < 32) tau_raw[tid] = tl;  // lane tid < 32 holds query col = tid
       }
+      int nh = 0;
+      if (whole) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nh += acc[r] >= tl ? 1 : 0;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          nh += (acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem) ? 1 : 0;
+      }
+      if (__any(nh != 0)) {
+        // One LDS atomic per lane reserves its entries; the writes then go out
+        // without waiting on each other: a lane without a hit at r writes to
+        // its spare slot past kScanCap, so branches stay uniform.
+        int o = nh ? atomicAdd(&cnt[col], nh) : 0;
+        wait_lds();
+        ScanEntry* bb = bucket + col * kScanStride;
+        const int spare = kScanCap + half;
+        const int j0 = (int)(blk + 4 * half);
+        if (whole) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool hit = acc[r] >= tl;
+            if (__any(hit)) {
+              ScanEntry* d = bb + (hit ? o : spare);
+              d->raw = acc[r];
+              d->j = j0 + 8 * (r >> 2) + (r & 3);
+              o += hit ? 1 : 0;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool hit = acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem;
+            if (__any(hit)) {
+              ScanEntry* d = bb + (hit ? o : spare);
+              d->raw = acc[r];
+              d->j = j0 + 8 * (r >> 2) + (r & 3);
+              o += hit ? 1 : 0;
+            }
+          }
+        }
+        // the last lane to append to a query sees its final count
+        if (nh && o > kScanCap - 128) full[round % 3] = 1;
+      }
+      __syncthreads();
+      if (round + 1 < n_rounds && full[round % 3])
+        scan_compact<KMAX>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
     }
-    __syncthreads();
   }
-  if (g == 0 && q_ok) {
-    const int64_t qrow = head * n_query + q;
-    if (nsplit == 1) {
+  scan_compact<KMAX>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
+
+  const int qs = tid >> 3, sub = tid & 7;
+  const int64_t qq = (int64_t)qt * 32 + qs;
+  if (qq >= n_query) return;
+  const int m = nkept[qs];
+  const int64_t qrow = head * n_query + qq;
+  if (nsplit == 1) {
+    if (sub == 0) {
+      float s[KMAX];
+      int id[KMAX];
+      keys_to_list<KMAX>(kept[qs], m, s, id);
       finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                            w_out + qrow * k);
-    } else {
-      float* ps = part_s + (qrow * nsplit + sp) * KMAX;
-      int32_t* pi = part_i + (qrow * nsplit + sp) * KMAX;
-#pragma unroll
-      for (int p = 0; p < KMAX; ++p) {
-        ps[p] = s[p];
-        pi[p] = id[p];
-      }
     }
+  } else {
+    uint64_t* dst = part + (qrow * nsplit + sp) * KMAX;
+    for (int p = sub; p < KMAX; p += 8) dst[p] = p < m ? kept[qs][p] : 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the per-slice lists.  One wave per (head, query), 4 per workgroup.
+// Merge of the per-slice lists: one wave per (head, query) row, n = nsplit *
+// KMAX keys (0 = empty).  The k-th largest of the 64 lane maxima bounds the
+// k-th best key from below; entries at or above it are packed into LDS and
+// ranked exactly.
 // ---------------------------------------------------------------------------
+constexpr int kMergeMax = 4096;  // nsplit * KMAX limit (LDS list size)
+
 template <int KMAX>
-__global__ __launch_bounds__(256) void k_topk_merge(
-    const float* __restrict__ part_s, const int32_t* __restrict__ part_i, int64_t n_rows,
-    int nsplit, int k, int softmax_one, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, float* __restrict__ w_out) {
-  __shared__ float ls[4][64][KMAX];
-  __shared__ int li[4][64][KMAX];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t qrow = (int64_t)blockIdx.x * 4 + wave;
-  const bool ok = qrow < n_rows;
-  float s[KMAX];
-  int id[KMAX];
-  list_clear(s, id);
-  if (ok) {
-    const int64_t n = (int64_t)nsplit * KMAX;
-    const float* ps = part_s + qrow * n;
-    const int32_t* pi = part_i + qrow * n;
-    for (int64_t e = lane; e < n; e += 64) {
-      const float x = ps[e];
-      const int j = pi[e];
-      if (j != kIdxNone && better(x, j, s[KMAX - 1], id[KMAX - 1])) list_insert(s, id, x, j);
-    }
-  }
+__global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ part, int n,
+                                                   int k, int softmax_one,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ score_out,
+                                                   float* __restrict__ w_out) {
+  __shared__ uint64_t lst[kMergeMax];
+  __shared__ uint64_t out[KMAX];
+  const int lane = threadIdx.x;
+  const int64_t qrow = blockIdx.x;
+  const uint64_t* src = part + qrow * n;
+
+  uint64_t mx = 0;
+  for (int e0 = 0; e0 < n; e0 += 256) {
+    uint64_t v[4];
 #pragma unroll
-  for (int p = 0; p < KMAX; ++p) {
-    ls[wave][lane][p] = s[p];
-    li[wave][lane][p] = id[p];
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + lane + 64 * u;
+      v[u] = src[e < n ? e : n - 1];
+      v[u] = e < n ? v[u] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mx = umax64(mx, v[u]);
+  }
+  // rank of this lane's maximum among the 64 (ties between empty lanes broken
+  // by lane number), then the maximum of rank k-1
+  int rank = 0;
+#pragma unroll
+  for (int l = 0; l < 64; ++l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mx, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mx >> 32), l);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    rank += (o > mx || (o == mx && l < lane)) ? 1 : 0;
+  }
+  const uint64_t sel = __ballot(rank == k - 1);
+  const int src_lane = __builtin_ctzll(sel);  // k <= 16 < 64: exactly one lane
+  const uint32_t thr_hi = __builtin_amdgcn_readlane((uint32_t)(mx >> 32), src_lane);
+  const uint32_t thr_lo = __builtin_amdgcn_readlane((uint32_t)mx, src_lane);
+  const uint64_t thr = ((uint64_t)thr_hi << 32) | thr_lo;
+
+  int n2 = 0;
+  for (int e0 = 0; e0 < n; e0 += 256) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + lane + 64 * u;
+      v[u] = src[e < n ? e : n - 1];
+      v[u] = e < n ? v[u] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool pass = v[u] != 0 && v[u] >= thr;
+      const uint64_t mask = __ballot(pass);
+      const int pos = n2 + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      if (pass) lst[pos] = v[u];
+      n2 += __builtin_popcountll(mask);
+    }
   }
   __syncthreads();
-#pragma unroll
-  for (int step = 1; step < 64; step <<= 1) {
-    if ((lane % (2 * step)) == 0) {
-      merge_lists<KMAX>(ls[wave][lane], li[wave][lane], ls[wave][lane + step],
-                        li[wave][lane + step], s, id);
-#pragma unroll
-      for (int p = 0; p < KMAX; ++p) {
-        ls[wave][lane][p] = s[p];
-        li[wave][lane][p] = id[p];
-      }
-    }
-    __syncthreads();
+  for (int i = lane; i < n2; i += 64) {
+    const uint64_t me = lst[i];
+    int r = 0;
+    for (int f = 0; f < n2; ++f) r += lst[f] > me ? 1 : 0;
+    if (r < k) out[r] = me;
   }
-  if (ok && lane == 0)
+  __syncthreads();
+  if (lane == 0) {
+    float s[KMAX];
+    int id[KMAX];
+    keys_to_list<KMAX>(out, n2 < k ? n2 : k, s, id);
     finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                          w_out + qrow * k);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -313,20 +581,19 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
       hipLaunchKernelGGL((k_scan_topk_bf16<64, KMAX>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,
-                         a.softmax_one, a.idx, a.score, a.w, a.part_s, a.part_i);
+                         a.softmax_one, a.idx, a.score, a.w, a.part);
     else
       hipLaunchKernelGGL((k_scan_topk_bf16<32, KMAX>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,
-                         a.softmax_one, a.idx, a.score, a.w, a.part_s, a.part_i);
+                         a.softmax_one, a.idx, a.score, a.w, a.part);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t rows = heads * a.n_query;
     KernelTimer timer(kKernMerge, a.stream);
-    hipLaunchKernelGGL((k_topk_merge<KMAX>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                       a.stream, a.part_s, a.part_i, rows, pl.nsplit, a.k, a.softmax_one, a.idx,
-                       a.score, a.w);
+    hipLaunchKernelGGL((k_topk_merge<KMAX>), dim3((unsigned)rows), dim3(64), 0, a.stream, a.part,
+                       pl.nsplit * KMAX, a.k, a.softmax_one, a.idx, a.score, a.w);
     return hipGetLastError();
   }
   const int64_t rows = heads * a.n_query;

@@ -151,3 +151,45 @@ def test_bf16_backward_is_deterministic():
         assert torch.equal(g1[key], g2[key]), key
     o2, lse2 = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def _ordered_landmarks(order, B, H, n_key, n_query, seed):
+    """Landmarks whose scores follow `order` along the chunk axis: lk_j = c_j * u and
+    lq = u for one direction u per head, so score_j = c_j <u, u> / sqrt(Dl).
+    'equal': c_j = 1 (every candidate ties); 'rising' / 'falling': c_j steps up / down
+    with j over 128 levels (runs of equal c_j, so ties appear too).  Components of u
+    are +-2^e / 8 with e in {0, -1, -2} and c_j has at most 8 significant bits, so every
+    product and partial sum is exact in bfloat16 inputs and float32 accumulation:
+    float32 and float64 scores agree bit for bit and ties are exact."""
+    rng = np.random.default_rng(seed)
+    sign = rng.choice([-1.0, 1.0], size=(1, B, H, 1, 64))
+    u = (sign * 2.0 ** -rng.integers(0, 3, size=(1, B, H, 1, 64)) / 8).astype(np.float32)
+    step = np.floor(np.arange(n_key) * 128 / n_key).astype(np.float32) / 128
+    c = {"equal": np.ones(n_key, np.float32), "rising": 1.0 + step, "falling": 2.0 - step}[order]
+    lk = torch.from_numpy((c[None, None, None, :, None] * u).astype(np.float32))
+    lq = torch.from_numpy(np.broadcast_to(u, (1, B, H, n_query, 64)).copy())
+    assert torch.equal(lk.bfloat16().float(), lk) and torch.equal(lq.bfloat16().float(), lq)
+    return lq.bfloat16(), lk.bfloat16()
+
+
+@pytest.mark.parametrize("order", ["equal", "rising", "falling"])
+@pytest.mark.parametrize("k", [8, 16])
+@pytest.mark.parametrize("sliced", [False, True])
+def test_bf16_scan_adversarial_orders(order, k, sliced):
+    """Score orders that defeat the running threshold (every candidate ties, or each
+    one beats all before it) or make it trivial; one slice and long slices."""
+    if sliced:  # 192 heads: 6000 candidates cut into a few slices of 12 rounds each
+        B, H, n_key, n_query = 16, 12, 6000, 3
+        q_pos = torch.tensor([6001, 6001, 3500], dtype=torch.int32)
+    else:
+        B, H, n_key, n_query = 1, 3, 700, 40
+        q_pos = torch.arange(n_query, dtype=torch.int32) * 18
+    cfg = synth.workload("retrieve16m", B=B, H=H, n_key=n_key, n_query=n_query, k=k)
+    lq, lk = _ordered_landmarks(order, B, H, n_key, n_query, seed=11 + k)
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(lq), dev(lk), dev(q_pos))
+    r_idx, r_score, r_w = orc.retrieve(f64(lq), f64(lk), q_pos.numpy(), k, cfg["score_scale"],
+                                       cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    close("score", f64(score), r_score, True)
+    close("w", f64(w), r_w, True)
