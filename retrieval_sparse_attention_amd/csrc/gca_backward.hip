@@ -174,8 +174,96 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
 // bf16 query-side backward (S = D = 64).  Four waves; wave w owns query rows
 // 16w .. 16w+15 on 16x16x32 MFMA tiles.  The next valid slot's K and V tiles
 // stream into the other half of a double-buffered swizzled LDS area while the
-// current slot is computed.
+// current slot is computed (asynchronous copies the compiler does not wait
+// on; the slot loop is unrolled by two so both buffers are fixed addresses).
 // ---------------------------------------------------------------------------
+struct BwdQCtx {
+  const TileDma<4>* dma;
+  const bf16* k_head;
+  const bf16* v_head;
+  const int* slot_c;   // LDS
+  const float* slot_w; // LDS
+  const int* s_list;   // LDS: valid slots in order
+  float (*dw_part)[16];  // LDS [4][16]
+  const float* lse_row;  // lse + tile * topk * 64 + x
+  float* delta_row;      // delta + tile * topk * 64 + x
+  int n, lane, wave, grp, col;
+  float c2;
+};
+
+__device__ __forceinline__ void bwdq_issue(const BwdQCtx& cx, int u, bf16* __restrict__ kd,
+                                           bf16* __restrict__ vd) {
+  const int64_t c = uniform(cx.slot_c[uniform(cx.s_list[u])]);
+  cx.dma->copy_async(kd, cx.k_head + c * 4096);
+  cx.dma->copy_async(vd, cx.v_head + c * 4096);
+}
+
+__device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_next,
+                                          const bf16x8 (&bq)[2], const bf16x8 (&bdo)[2],
+                                          f32x4 (&dqacc)[4], const bf16* __restrict__ kt,
+                                          const bf16* __restrict__ vt, bf16* __restrict__ kn,
+                                          bf16* __restrict__ vn) {
+  const int lane = cx.lane, grp = cx.grp, col = cx.col;
+  const int i = uniform(cx.s_list[u]);
+  const float wi = cx.slot_w[i];
+  wait_vmem();
+  __syncthreads();
+  // the next slot's log-sum-exp row is loaded raw and scaled only here, after
+  // the wait: using it earlier would drain the tile copies issued with it
+  const float l2 = l2_next * kLog2e;
+  if (u + 1 < cx.n) {
+    bwdq_issue(cx, u + 1, kn, vn);
+    l2_next = cx.lse_row[uniform(cx.s_list[u + 1]) * 64];
+  }
+  // S^T = K Q^T and dP~^T = V dO^T per key tile mt; lane holds keys 16mt + 4grp + r.
+  f32x4 sacc[4], pacc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    sacc[mt] = zero4();
+    pacc[mt] = zero4();
+#pragma unroll
+    for (int kd = 0; kd < 2; ++kd) {
+      sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
+      pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
+    }
+  }
+  // K^T operands of this slot, requested now so that the LDS latency overlaps
+  // the elementwise arithmetic below.
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+  float dp[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    dp[mt] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(fmaf(sacc[mt][r], cx.c2, -l2));
+      sacc[mt][r] = p;
+      dp[mt] = fmaf(p, pacc[mt][r], dp[mt]);
+    }
+  }
+  const float dsum = xor32_sum(xor16_sum((dp[0] + dp[1]) + (dp[2] + dp[3])));
+  if (grp == 0) cx.delta_row[i * 64] = dsum;
+  const float part = row16_sum(dsum);  // the 16 query rows of this wave
+  if (lane == 0) cx.dw_part[cx.wave][i] = part;
+  // dS^T = w P (dP~ - D); dQ^T (d x x) += K^T (d x j) dS^T (j x x)
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    bf16x8 bs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bs[e] = (bf16)(wi * sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
+      bs[4 + e] = (bf16)(wi * sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
@@ -227,79 +315,37 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
     }
   }
   f32x4 dqacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  const float c2 = attn_scale * kLog2e;
+  const TileDma<4> dma(wave, lane);
+  BwdQCtx cx;
+  cx.dma = &dma;
+  cx.k_head = kk + head * n_key * 4096;
+  cx.v_head = v + head * n_key * 4096;
+  cx.slot_c = slot_c;
+  cx.slot_w = slot_w;
+  cx.s_list = s_list;
+  cx.dw_part = dw_part;
+  cx.lse_row = lse + tile * topk * 64 + x;
+  cx.delta_row = delta + tile * topk * 64 + x;
+  cx.lane = lane;
+  cx.wave = wave;
+  cx.grp = grp;
+  cx.col = col;
+  cx.c2 = attn_scale * kLog2e;
   __syncthreads();
-  const int n = s_n;
+  const int n = uniform(s_n);
+  cx.n = n;
   if (grp == 0)
     for (int i = 0; i < topk; ++i)
-      if (!((s_mask >> i) & 1)) delta[(tile * topk + i) * 64 + x] = 0.0f;
+      if (!((s_mask >> i) & 1)) cx.delta_row[i * 64] = 0.0f;
   float l2_next = 0.0f;
   if (n > 0) {
-    const int i0 = s_list[0];
-    tile_dma<4>(k_lds[0], kk + (head * n_key + slot_c[i0]) * 4096, wave, lane);
-    tile_dma<4>(v_lds[0], v + (head * n_key + slot_c[i0]) * 4096, wave, lane);
-    l2_next = lse[(tile * topk + i0) * 64 + x] * kLog2e;
+    bwdq_issue(cx, 0, k_lds[0], v_lds[0]);
+    l2_next = cx.lse_row[uniform(s_list[0]) * 64];
   }
-  for (int u = 0; u < n; ++u) {
-    const int buf = u & 1;
-    const int i = s_list[u];
-    const float wi = slot_w[i];
-    wait_vmem();
-    __syncthreads();
-    const float l2 = l2_next;
-    if (u + 1 < n) {
-      const int i1 = s_list[u + 1];
-      tile_dma<4>(k_lds[buf ^ 1], kk + (head * n_key + slot_c[i1]) * 4096, wave, lane);
-      tile_dma<4>(v_lds[buf ^ 1], v + (head * n_key + slot_c[i1]) * 4096, wave, lane);
-      l2_next = lse[(tile * topk + i1) * 64 + x] * kLog2e;
-    }
-    const bf16* kt = k_lds[buf];
-    const bf16* vt = v_lds[buf];
-    // S^T = K Q^T and dP~^T = V dO^T per key tile mt; lane holds keys 16mt + 4grp + r.
-    f32x4 sacc[4], pacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = zero4();
-      pacc[mt] = zero4();
-#pragma unroll
-      for (int kd = 0; kd < 2; ++kd) {
-        sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
-        pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
-      }
-    }
-    // K^T operands of this slot, requested now so that the LDS latency overlaps
-    // the elementwise arithmetic below.
-    bf16x8 ka[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-    float dsum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(sacc[mt][r], c2, -l2));
-        sacc[mt][r] = p;
-        dsum = fmaf(p, pacc[mt][r], dsum);
-      }
-    dsum = xor32_sum(xor16_sum(dsum));
-    if (grp == 0) delta[(tile * topk + i) * 64 + x] = dsum;
-    const float part = row16_sum(dsum);  // the 16 query rows of this wave
-    if (lane == 0) dw_part[wave][i] = part;
-    // dS^T = w P (dP~ - D); dQ^T (d x x) += K^T (d x j) dS^T (j x x)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 bs;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bs[e] = (bf16)(wi * sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
-        bs[4 + e] = (bf16)(wi * sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
-    }
+  for (int u = 0; u < n; u += 2) {
+    bwdq_slot(cx, u, l2_next, bq, bdo, dqacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
+    if (u + 1 < n)
+      bwdq_slot(cx, u + 1, l2_next, bq, bdo, dqacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
   }
   bf16* dqrow = dq + tile * 4096 + x * 64 + 4 * grp;
 #pragma unroll
@@ -320,11 +366,120 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
 // ---------------------------------------------------------------------------
 // bf16 key-side backward (S = D = 64).  Four waves; wave w owns key rows
 // 16w .. 16w+15 on 16x16x32 MFMA tiles.  The reverse-list entries are staged
-// in LDS 128 at a time; the next entry's Q and dO tiles stream into the other
-// half of a double-buffered swizzled LDS area and its log-sum-exp / D rows and
-// scalars into registers while the current entry is computed.  The 64 query
-// rows of a pair are processed as two 32-row contraction steps.
+// in LDS 256 at a time; the next entry's Q and dO tiles stream into the other
+// half of a double-buffered swizzled LDS area (asynchronous copies) and its
+// log-sum-exp / D rows and scalars into registers while the current entry is
+// computed.  The 64 query rows of a pair are processed as two 32-row
+// contraction steps; the entry loop is unrolled by two so both buffers are
+// fixed LDS addresses.
 // ---------------------------------------------------------------------------
+struct BwdKVCtx {
+  const TileDma<4>* dma;
+  const bf16* q_head;     // q + head * n_query * 4096
+  const bf16* do_head;    // dout + head * n_query * 4096
+  const float* lse_head;  // lse + pair0 * 64
+  const float* d_head;    // delta + pair0 * 64
+  const float* w_head;    // w + pair0
+  const float* ds_head;   // dscore + pair0
+  const bf16* lq_head;    // lq + head * n_query * dl, or NULL
+  const int* s_ent;       // LDS
+  int topk, dl, tid, lane, grp, col;
+  float c2;
+};
+
+// Registers that carry one entry's scalars from its fetch to its use, raw as
+// loaded: converting them at fetch time would make the compiler wait for the
+// loads there, and with them for the tile copies issued just before.
+struct KVNext {
+  float row, w, ds;
+  bf16 lq;
+};
+
+__device__ __forceinline__ void bwdkv_fetch(const BwdKVCtx& cx, int u, KVNext& nx,
+                                            bf16* __restrict__ qd, bf16* __restrict__ dod) {
+  const int ent = uniform(cx.s_ent[u]);
+  const int t = ent / cx.topk;
+  cx.dma->copy_async(qd, cx.q_head + (int64_t)t * 4096);
+  cx.dma->copy_async(dod, cx.do_head + (int64_t)t * 4096);
+  const int tid = cx.tid;
+  if (tid < 128)
+    nx.row = tid < 64 ? cx.lse_head[(int64_t)ent * 64 + tid]
+                      : cx.d_head[(int64_t)ent * 64 + (tid - 64)];
+  nx.w = cx.w_head[ent];
+  if (cx.lq_head) {
+    nx.ds = cx.ds_head[ent];
+    nx.lq = cx.lq_head[(int64_t)t * cx.dl + (tid < cx.dl ? tid : 0)];
+  }
+}
+
+__device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, KVNext& nx,
+                                            float& dlk_acc, const bf16x8 (&bk)[2],
+                                            const bf16x8 (&bv)[2], f32x4 (&dkacc)[4],
+                                            f32x4 (&dvacc)[4], const bf16* __restrict__ qt,
+                                            const bf16* __restrict__ dot, float* __restrict__ l2r,
+                                            float* __restrict__ dr, bf16* __restrict__ qn,
+                                            bf16* __restrict__ don) {
+  const int lane = cx.lane, grp = cx.grp, col = cx.col, tid = cx.tid;
+  wait_vmem();
+  if (tid < 64)
+    l2r[tid] = nx.row * kLog2e;
+  else if (tid < 128)
+    dr[tid - 64] = nx.row;
+  const float wi = nx.w;
+  if (cx.lq_head && tid < cx.dl) dlk_acc = fmaf(nx.ds, (float)nx.lq, dlk_acc);
+  __syncthreads();
+  if (u + 1 < nb) bwdkv_fetch(cx, u + 1, nx, qn, don);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // dO^T and Q^T operands of this contraction step, requested first so
+    // that their LDS latency overlaps the products and arithmetic below.
+    bf16x8 ado[4], aq[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      ado[dt] = lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      aq[dt] = lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+    }
+    // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query tiles 2kb, 2kb+1;
+    // the lane holds rows x = 32kb + 16h + 4grp + r of its key column j.
+    f32x4 sacc[2], pacc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int xr = 32 * kb + 16 * h + col;
+      sacc[h] = zero4();
+      pacc[h] = zero4();
+#pragma unroll
+      for (int kd = 0; kd < 2; ++kd) {
+        sacc[h] = mfma16x16x32(lds_row8(qt, xr, 4 * kd + grp), bk[kd], sacc[h]);
+        pacc[h] = mfma16x16x32(lds_row8(dot, xr, 4 * kd + grp), bv[kd], pacc[h]);
+      }
+      // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
+      const int x0 = 32 * kb + 16 * h + 4 * grp;
+      const f32x4 l4 = *(const f32x4*)(l2r + x0);
+      const f32x4 d4 = *(const f32x4*)(dr + x0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pw = wi * fast_exp2(fmaf(sacc[h][e], cx.c2, -l4[e]));
+        sacc[h][e] = pw;
+        pacc[h][e] = pw * (pacc[h][e] - d4[e]);
+      }
+    }
+    // dV^T (d x j) += dO^T (d x x) P_w (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
+    bf16x8 bp, bs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bp[e] = (bf16)sacc[0][e];
+      bp[4 + e] = (bf16)sacc[1][e];
+      bs[e] = (bf16)pacc[0][e];
+      bs[4 + e] = (bf16)pacc[1][e];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      dvacc[dt] = mfma16x16x32(ado[dt], bp, dvacc[dt]);
+      dkacc[dt] = mfma16x16x32(aq[dt], bs, dkacc[dt]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
@@ -358,97 +513,42 @@ __global__ __launch_bounds__(256) void k_bwd_kv_bf16(
   f32x4 dkacc[4] = {zero4(), zero4(), zero4(), zero4()};
   f32x4 dvacc[4] = {zero4(), zero4(), zero4(), zero4()};
   float dlk_acc = 0.0f;
-  const float c2 = attn_scale * kLog2e;
   const int beg = rev_off[head * (n_key + 1) + c];
   const int end = rev_off[head * (n_key + 1) + c + 1];
   const int32_t* ents = rev_ent + head * n_query * topk;
   const int64_t pair0 = head * n_query * topk;
+  const TileDma<4> dma(wave, lane);
+  BwdKVCtx cx;
+  cx.dma = &dma;
+  cx.q_head = q + head * n_query * 4096;
+  cx.do_head = dout + head * n_query * 4096;
+  cx.lse_head = lse + pair0 * 64;
+  cx.d_head = delta + pair0 * 64;
+  cx.w_head = w + pair0;
+  cx.ds_head = dscore + pair0;
+  cx.lq_head = lq ? lq + head * n_query * dl : nullptr;
+  cx.s_ent = s_ent;
+  cx.topk = topk;
+  cx.dl = dl;
+  cx.tid = tid;
+  cx.lane = lane;
+  cx.grp = grp;
+  cx.col = col;
+  cx.c2 = attn_scale * kLog2e;
 
   for (int b0 = beg; b0 < end; b0 += 256) {
     const int nb = (end - b0) < 256 ? (end - b0) : 256;
     __syncthreads();  // every wave is done with the previous block
     if (tid < nb) s_ent[tid] = ents[b0 + tid];
     __syncthreads();
-    float rrow = 0.0f, rw = 0.0f, rds = 0.0f, rlq = 0.0f;
-    auto fetch = [&](int u, int buf) {
-      const int ent = s_ent[u];
-      const int64_t t = ent / topk;
-      const int64_t pair = pair0 + ent;
-      tile_dma<4>(q_lds[buf], q + (head * n_query + t) * 4096, wave, lane);
-      tile_dma<4>(do_lds[buf], dout + (head * n_query + t) * 4096, wave, lane);
-      if (tid < 128)
-        rrow = tid < 64 ? lse[pair * 64 + tid] * kLog2e : delta[pair * 64 + (tid - 64)];
-      rw = w[pair];
-      if (lq) {
-        rds = dscore[pair];
-        rlq = tid < dl ? (float)lq[(head * n_query + t) * dl + tid] : 0.0f;
-      }
-    };
-    fetch(0, 0);
-    for (int u = 0; u < nb; ++u) {
-      const int buf = u & 1;
-      wait_vmem();
-      if (tid < 64)
-        l2_lds[buf][tid] = rrow;
-      else if (tid < 128)
-        d_lds[buf][tid - 64] = rrow;
-      const float wi = rw;
-      dlk_acc = fmaf(rds, rlq, dlk_acc);
-      __syncthreads();
-      if (u + 1 < nb) fetch(u + 1, buf ^ 1);
-      const bf16* qt = q_lds[buf];
-      const bf16* dot = do_lds[buf];
-      const float* l2r = l2_lds[buf];
-      const float* dr = d_lds[buf];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // dO^T and Q^T operands of this contraction step, requested first so
-        // that their LDS latency overlaps the products and arithmetic below.
-        bf16x8 ado[4], aq[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          ado[dt] = lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-          aq[dt] = lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-        }
-        // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query tiles 2kb, 2kb+1;
-        // the lane holds rows x = 32kb + 16h + 4grp + r of its key column j.
-        f32x4 sacc[2], pacc[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int xr = 32 * kb + 16 * h + col;
-          sacc[h] = zero4();
-          pacc[h] = zero4();
-#pragma unroll
-          for (int kd = 0; kd < 2; ++kd) {
-            sacc[h] = mfma16x16x32(lds_row8(qt, xr, 4 * kd + grp), bk[kd], sacc[h]);
-            pacc[h] = mfma16x16x32(lds_row8(dot, xr, 4 * kd + grp), bv[kd], pacc[h]);
-          }
-          // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
-          const int x0 = 32 * kb + 16 * h + 4 * grp;
-          const f32x4 l4 = *(const f32x4*)(l2r + x0);
-          const f32x4 d4 = *(const f32x4*)(dr + x0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pw = wi * fast_exp2(fmaf(sacc[h][e], c2, -l4[e]));
-            sacc[h][e] = pw;
-            pacc[h][e] = pw * (pacc[h][e] - d4[e]);
-          }
-        }
-        // dV^T (d x j) += dO^T (d x x) P_w (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
-        bf16x8 bp, bs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bp[e] = (bf16)sacc[0][e];
-          bp[4 + e] = (bf16)sacc[1][e];
-          bs[e] = (bf16)pacc[0][e];
-          bs[4 + e] = (bf16)pacc[1][e];
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dvacc[dt] = mfma16x16x32(ado[dt], bp, dvacc[dt]);
-          dkacc[dt] = mfma16x16x32(aq[dt], bs, dkacc[dt]);
-        }
-      }
+    KVNext nx{0.0f, 0.0f, 0.0f, (bf16)0.0f};
+    bwdkv_fetch(cx, 0, nx, q_lds[0], do_lds[0]);
+    for (int u = 0; u < nb; u += 2) {
+      bwdkv_entry(cx, u, nb, nx, dlk_acc, bk, bv, dkacc, dvacc, q_lds[0], do_lds[0], l2_lds[0],
+                  d_lds[0], q_lds[1], do_lds[1]);
+      if (u + 1 < nb)
+        bwdkv_entry(cx, u + 1, nb, nx, dlk_acc, bk, bv, dkacc, dvacc, q_lds[1], do_lds[1],
+                    l2_lds[1], d_lds[1], q_lds[0], do_lds[0]);
     }
   }
   bf16* dkrow = dk + tile * 4096 + j * 64 + 4 * grp;

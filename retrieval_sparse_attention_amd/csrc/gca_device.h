@@ -189,6 +189,65 @@ __device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* __restrict_
   }
 }
 
+// The same copy with the per-lane part of the addresses computed once: `off`
+// holds, for each of the wave's 8/NW pieces, this lane's byte offset inside
+// the source tile, so a copy costs no vector arithmetic when the tile base is
+// wave-uniform (it is then used as the scalar base of global_load_lds).
+template <int NW>
+struct TileDma {
+  uint32_t off[8 / NW];
+  int first_piece;
+  __device__ __forceinline__ TileDma(int wave, int lane) : first_piece(wave * (8 / NW)) {
+#pragma unroll
+    for (int r = 0; r < 8 / NW; ++r) {
+      const int row = (first_piece + r) * 8 + (lane >> 3), pc = lane & 7;
+      off[r] = (uint32_t)(row * 64 + ((pc ^ (row & 7)) << 3)) * 2u;
+    }
+  }
+  __device__ __forceinline__ void copy(bf16* lds_tile, const bf16* src) const {
+    const char* base = (const char*)src;
+#pragma unroll
+    for (int r = 0; r < 8 / NW; ++r)
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[r]),
+                                       (lds_void*)(lds_tile + (first_piece + r) * 512), 16, 0, 0);
+  }
+  // Same copy issued as plain instructions the compiler does not interpret:
+  // it then never waits for the copy before unrelated LDS reads (it cannot
+  // tell the destination apart from the tile being read and would otherwise
+  // drain the copy right away).  The caller owns the wait: wait_vmem() and a
+  // barrier before the tile is read.  `src` must be wave-uniform; M0 is
+  // restored afterwards.
+  __device__ __forceinline__ void copy_async(bf16* lds_tile, const bf16* src) const {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds_tile;
+#pragma unroll
+    for (int r = 0; r < 8 / NW; ++r) {
+      const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(lds0 + (uint32_t)(first_piece + r) * 1024u));
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %2, %3\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(dst), "v"(off[r]), "s"(src)
+          : "memory");
+    }
+  }
+};
+
+// Wave-uniform copy of an int read from LDS (lets the compiler keep it scalar).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Approximate reciprocal (v_rcp_f32, about 1 ulp) and natural log through the
+// hardware log2 (v_log_f32, about 1 ulp); both are far inside the bf16
+// accuracy of the attention path.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_ln(float x) {
+  return __builtin_amdgcn_logf(x) * 0.69314718055994531f;
+}
+
 // s_waitcnt vmcnt(0): every vector memory access of this wave has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -10,8 +10,10 @@
 // retrieved chunk:
 //   1. the K and V tiles (8 KB each) of the next retrieved chunk stream from
 //      global memory straight into the other half of a double-buffered,
-//      XOR-swizzled LDS area (global_load_lds) while the current chunk is
-//      computed; one barrier per chunk;
+//      XOR-swizzled LDS area (global_load_lds, scalar tile base plus per-lane
+//      offsets computed once) while the current chunk is computed; one barrier
+//      per chunk, and the chunk loop is unrolled by two so that both buffers
+//      are fixed LDS addresses;
 //   2. S^T = K Q^T on MFMA (A = K rows from LDS, B = Q^T kept in registers), so a
 //      lane holds 16 of the 64 logits of ONE query row and the lanes l ^ 16,
 //      l ^ 32, l ^ 48 the others: the row max and row sum need two exchanges;
@@ -30,6 +32,96 @@
 #include "gca_launch.h"
 
 namespace gca {
+
+// Per-workgroup state of the bf16 forward shared by its chunk steps.
+struct FwdCtx {
+  const TileDma<4>* dma;
+  const bf16* k_head;
+  const bf16* v_head;
+  const int* s_c;      // LDS: chunk of each valid slot
+  const float* s_w;    // LDS: its fusion weight
+  const int* s_slot;   // LDS: its slot number
+  float* lse_row;      // lse + (tile * topk) * 64 + x, or unused
+  bool want_lse;
+  int n, lane, grp, col;
+  float c2, attn_scale;
+};
+
+// DMA of the K and V tiles of valid slot u into kd / vd.
+__device__ __forceinline__ void fwd_issue(const FwdCtx& cx, int u, bf16* __restrict__ kd,
+                                          bf16* __restrict__ vd) {
+  const int64_t c = uniform(cx.s_c[u]);
+  cx.dma->copy_async(kd, cx.k_head + c * 4096);
+  cx.dma->copy_async(vd, cx.v_head + c * 4096);
+}
+
+// One retrieved chunk: kt/vt hold its tiles; the next chunk's tiles are sent
+// to kn/vn.  The restrict qualifiers tell the compiler that the LDS reads of
+// this chunk never touch the buffers being filled, so it does not wait for
+// that copy before reading (it would otherwise drain the copy at once).
+__device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 (&bq)[2],
+                                          f32x4 (&oacc)[4], const bf16* __restrict__ kt,
+                                          const bf16* __restrict__ vt, bf16* __restrict__ kn,
+                                          bf16* __restrict__ vn) {
+  const int lane = cx.lane, grp = cx.grp, col = cx.col;
+  wait_vmem();
+  __syncthreads();  // tiles of slot u are in LDS; slot u-1 is done with the other buffer
+  if (u + 1 < cx.n) fwd_issue(cx, u + 1, kn, vn);
+  // S^T = K Q^T: key tile mt (16 keys) x this wave's 16 queries; the lane
+  // holds keys 16mt + 4*grp + r of its query column x.
+  f32x4 sacc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    sacc[mt] = zero4();
+#pragma unroll
+    for (int kd = 0; kd < 2; ++kd)
+      sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
+  }
+  // V^T operands of this slot, requested now so that the LDS latency overlaps
+  // the softmax arithmetic below.
+  bf16x8 va[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      va[kb][dt] = lds_tr_operand16(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+  float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
+  m = xor32_max(xor16_max(m));
+  const float mb = m * cx.c2;
+  float lp[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    lp[mt] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
+      sacc[mt][r] = e;
+      lp[mt] += e;
+    }
+  }
+  const float l = xor32_sum(xor16_sum((lp[0] + lp[1]) + (lp[2] + lp[3])));
+  if (cx.want_lse && grp == 0)
+    cx.lse_row[uniform(cx.s_slot[u]) * 64] = cx.attn_scale * m + fast_ln(l);
+  const float ps = cx.s_w[u] * fast_rcp(l);
+
+  // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step kb covers keys
+  // 32kb + 4*grp + 0..3 (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile
+  // 2kb+1): exactly what this lane holds; V^T comes by transpose reads.
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    bf16x8 bp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bp[e] = (bf16)(sacc[2 * kb][e] * ps);
+      bp[4 + e] = (bf16)(sacc[2 * kb + 1][e] * ps);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma16x16x32(va[kb][dt], bp, oacc[dt]);
+  }
+}
 
 __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
@@ -73,77 +165,32 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
     for (int kd = 0; kd < 2; ++kd) bq[kd] = *(const bf16x8*)(row + 32 * kd);
   }
   f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  const float c2 = attn_scale * kLog2e;
+  const TileDma<4> dma(wave, lane);
+  FwdCtx cx;
+  cx.dma = &dma;
+  cx.k_head = kk + head * n_key * 4096;
+  cx.v_head = v + head * n_key * 4096;
+  cx.s_c = s_c;
+  cx.s_w = s_w;
+  cx.s_slot = s_slot;
+  cx.lse_row = lse + tile * topk * 64 + x;
+  cx.want_lse = lse != nullptr;
+  cx.lane = lane;
+  cx.grp = grp;
+  cx.col = col;
+  cx.c2 = attn_scale * kLog2e;
+  cx.attn_scale = attn_scale;
   __syncthreads();
-  const int n = s_n;
+  const int n = uniform(s_n);
+  cx.n = n;
   if (lse && grp == 0)  // empty slots read lse = -inf
     for (int i = 0; i < topk; ++i)
-      if (!((s_mask >> i) & 1)) lse[(tile * topk + i) * 64 + x] = -__builtin_huge_valf();
-  if (n > 0) {
-    tile_dma<4>(k_lds[0], kk + (head * n_key + s_c[0]) * 4096, wave, lane);
-    tile_dma<4>(v_lds[0], v + (head * n_key + s_c[0]) * 4096, wave, lane);
-  }
-  for (int u = 0; u < n; ++u) {
-    const int buf = u & 1;
-    wait_vmem();
-    __syncthreads();  // tiles of slot u are in LDS; slot u-1 is done with the other buffer
-    if (u + 1 < n) {
-      tile_dma<4>(k_lds[buf ^ 1], kk + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
-      tile_dma<4>(v_lds[buf ^ 1], v + (head * n_key + s_c[u + 1]) * 4096, wave, lane);
-    }
-    const bf16* kt = k_lds[buf];
-    const bf16* vt = v_lds[buf];
-    // S^T = K Q^T: key tile mt (16 keys) x this wave's 16 queries; the lane
-    // holds keys 16mt + 4*grp + r of its query column x.
-    f32x4 sacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = zero4();
-#pragma unroll
-      for (int kd = 0; kd < 2; ++kd)
-        sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
-    }
-    // V^T operands of this slot, requested now so that the LDS latency overlaps
-    // the softmax arithmetic below.
-    bf16x8 va[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        va[kb][dt] = lds_tr_operand16(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-    float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
-#pragma unroll
-    for (int r = 1; r < 4; ++r)
-      m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
-    m = xor32_max(xor16_max(m));
-    const float mb = m * c2;
-    float l = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(fmaf(sacc[mt][r], c2, -mb));
-        sacc[mt][r] = e;
-        l += e;
-      }
-    l = xor32_sum(xor16_sum(l));
-    if (lse && grp == 0) lse[(tile * topk + s_slot[u]) * 64 + x] = attn_scale * m + logf(l);
-    const float ps = s_w[u] / l;
-
-    // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step kb covers keys
-    // 32kb + 4*grp + 0..3 (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile
-    // 2kb+1): exactly what this lane holds; V^T comes by transpose reads.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 bp;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bp[e] = (bf16)(sacc[2 * kb][e] * ps);
-        bp[4 + e] = (bf16)(sacc[2 * kb + 1][e] * ps);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma16x16x32(va[kb][dt], bp, oacc[dt]);
-    }
+      if (!((s_mask >> i) & 1)) cx.lse_row[i * 64] = -__builtin_huge_valf();
+  if (n > 0) fwd_issue(cx, 0, k_lds[0], v_lds[0]);
+  // unrolled by two: each step's buffers are fixed LDS addresses
+  for (int u = 0; u < n; u += 2) {
+    fwd_chunk(cx, u, bq, oacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
+    if (u + 1 < n) fwd_chunk(cx, u + 1, bq, oacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
   }
   // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
   bf16* orow = o + tile * 4096 + x * 64 + 4 * grp;
