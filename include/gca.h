@@ -172,7 +172,9 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
  *                                            w must come from gca_retrieve)
  *   dlq_t += score_scale sum_i dscore_i lk_c,   dlk_c += score_scale dscore_i lq_t
  * Top-k selection is treated as fixed.  Sums over (t, i) run in a fixed order,
- * so results are bitwise reproducible.
+ * so results are bitwise reproducible.  The bf16 path forms w_i P directly
+ * (log2 w_i joins the exponent); a slot whose weight is below about 1e-35
+ * (far below any contribution to dq, dk, dv or dscore) reports dw_i = 0.
  *
  *   q, dout        [G, B, H, Nq, S, D]  dtype, big
  *   k, v           [G, B, H, Nk, S, D]  dtype, big

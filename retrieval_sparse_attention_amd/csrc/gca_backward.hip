@@ -186,7 +186,8 @@ struct BwdQCtx {
   const int* s_list;   // LDS: valid slots in order
   float (*dw_part)[16];  // LDS [4][16]
   const float* lse_row;  // lse + tile * topk * 64 + x
-  float* delta_row;      // delta + tile * topk * 64 + x
+  float* s_delta;        // LDS [16][64]: D rows, written out at the end
+  int x;
   int n, lane, wave, grp, col;
   float c2;
 };
@@ -210,7 +211,9 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
   __syncthreads();
   // the next slot's log-sum-exp row is loaded raw and scaled only here, after
   // the wait: using it earlier would drain the tile copies issued with it
-  const float l2 = l2_next * kLog2e;
+  // P_w = w P comes out of the exponential directly: log2 w joins the row's
+  // offset (w = 0 gives P_w = 0 through exp2(-inf)).
+  const float l2 = l2_next * kLog2e - __builtin_amdgcn_logf(wi);
   if (u + 1 < cx.n) {
     bwdq_issue(cx, u + 1, kn, vn);
     l2_next = cx.lse_row[uniform(cx.s_list[u + 1]) * 64];
@@ -241,13 +244,15 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
     dp[mt] = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(fmaf(sacc[mt][r], cx.c2, -l2));
+      const float p = fast_exp2(fmaf(sacc[mt][r], cx.c2, -l2));  // = w P
       sacc[mt][r] = p;
       dp[mt] = fmaf(p, pacc[mt][r], dp[mt]);
     }
   }
-  const float dsum = xor32_sum(xor16_sum((dp[0] + dp[1]) + (dp[2] + dp[3])));
-  if (grp == 0) cx.delta_row[i * 64] = dsum;
+  // D = rowsum(P dP~) = rowsum(P_w dP~) / w  (0 when w = 0: P_w is 0 there)
+  const float dsw = xor32_sum(xor16_sum((dp[0] + dp[1]) + (dp[2] + dp[3])));
+  const float dsum = wi > 0.0f ? dsw * fast_rcp(wi) : 0.0f;
+  if (grp == 0) cx.s_delta[i * 64 + cx.x] = dsum;
   const float part = row16_sum(dsum);  // the 16 query rows of this wave
   if (lane == 0) cx.dw_part[cx.wave][i] = part;
   // dS^T = w P (dP~ - D); dQ^T (d x x) += K^T (d x j) dS^T (j x x)
@@ -256,8 +261,8 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
     bf16x8 bs;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bs[e] = (bf16)(wi * sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
-      bs[4 + e] = (bf16)(wi * sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
+      bs[e] = (bf16)(sacc[2 * kb][e] * (pacc[2 * kb][e] - dsum));
+      bs[4 + e] = (bf16)(sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
@@ -281,11 +286,15 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
   __shared__ int s_list[16];
   __shared__ int s_n;
   __shared__ int s_mask;
+  // D rows of the k slots, staged here and stored once at the end: a store per
+  // slot would be waited on by the next slot's copy wait.
+  __shared__ float s_delta[16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int64_t head = tile / n_query;
   const int x = 16 * wave + col;
+  for (int e = tid; e < topk * 64; e += 256) s_delta[e] = 0.0f;  // empty slots
 
   if (wave == 0) {  // slot table and compact list of the valid slots, in one step
     const int i = lane < topk ? lane : 0;
@@ -325,7 +334,8 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
   cx.s_list = s_list;
   cx.dw_part = dw_part;
   cx.lse_row = lse + tile * topk * 64 + x;
-  cx.delta_row = delta + tile * topk * 64 + x;
+  cx.s_delta = s_delta;
+  cx.x = x;
   cx.lane = lane;
   cx.wave = wave;
   cx.grp = grp;
@@ -334,9 +344,6 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
   __syncthreads();
   const int n = uniform(s_n);
   cx.n = n;
-  if (grp == 0)
-    for (int i = 0; i < topk; ++i)
-      if (!((s_mask >> i) & 1)) cx.delta_row[i * 64] = 0.0f;
   float l2_next = 0.0f;
   if (n > 0) {
     bwdq_issue(cx, 0, k_lds[0], v_lds[0]);
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16(
     *(bf16x4*)(dqrow + 16 * dt) = val;
   }
   __syncthreads();
+  for (int e = tid; e < topk * 64; e += 256) delta[tile * topk * 64 + e] = s_delta[e];
   if (tid < topk) dw_slot[tid] = (dw_part[0][tid] + dw_part[1][tid]) + (dw_part[2][tid] + dw_part[3][tid]);
   __syncthreads();
   score_epilogue<bf16>(tid, 256, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
@@ -421,11 +429,12 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
                                             bf16* __restrict__ don) {
   const int lane = cx.lane, grp = cx.grp, col = cx.col, tid = cx.tid;
   wait_vmem();
+  // P_w = w P comes out of the exponential directly: log2 w joins the row
+  // offset (w = 0 gives P_w = 0 through exp2(-inf)).
   if (tid < 64)
-    l2r[tid] = nx.row * kLog2e;
+    l2r[tid] = nx.row * kLog2e - __builtin_amdgcn_logf(nx.w);
   else if (tid < 128)
     dr[tid - 64] = nx.row;
-  const float wi = nx.w;
   if (cx.lq_head && tid < cx.dl) dlk_acc = fmaf(nx.ds, (float)nx.lq, dlk_acc);
   __syncthreads();
   if (u + 1 < nb) bwdkv_fetch(cx, u + 1, nx, qn, don);
@@ -458,7 +467,7 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
       const f32x4 d4 = *(const f32x4*)(dr + x0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pw = wi * fast_exp2(fmaf(sacc[h][e], cx.c2, -l4[e]));
+        const float pw = fast_exp2(fmaf(sacc[h][e], cx.c2, -l4[e]));
         sacc[h][e] = pw;
         pacc[h][e] = pw * (pacc[h][e] - d4[e]);
       }

@@ -41,8 +41,8 @@ struct FwdCtx {
   const int* s_c;      // LDS: chunk of each valid slot
   const float* s_w;    // LDS: its fusion weight
   const int* s_slot;   // LDS: its slot number
-  float* lse_row;      // lse + (tile * topk) * 64 + x, or unused
-  bool want_lse;
+  float* s_lse;        // LDS [16][64]: log-sum-exp rows, written out at the end
+  int x;
   int n, lane, grp, col;
   float c2, attn_scale;
 };
@@ -103,8 +103,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
     }
   }
   const float l = xor32_sum(xor16_sum((lp[0] + lp[1]) + (lp[2] + lp[3])));
-  if (cx.want_lse && grp == 0)
-    cx.lse_row[uniform(cx.s_slot[u]) * 64] = cx.attn_scale * m + fast_ln(l);
+  if (grp == 0) cx.s_lse[uniform(cx.s_slot[u]) * 64 + cx.x] = cx.attn_scale * m + fast_ln(l);
   const float ps = cx.s_w[u] * fast_rcp(l);
 
   // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step kb covers keys
@@ -134,11 +133,15 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
   __shared__ int s_slot[16];
   __shared__ int s_n;
   __shared__ int s_mask;
+  // Log-sum-exp rows of the k slots, staged here and stored once at the end:
+  // a store per chunk would be waited on by the next chunk's copy wait.
+  __shared__ float s_lse[16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
   const int64_t head = tile / n_query;
   const int x = 16 * wave + col;  // query row owned by this lane
+  for (int e = tid; e < topk * 64; e += 256) s_lse[e] = -__builtin_huge_valf();  // empty slots
 
   // compact list of the valid slots, built in one step from a wave ballot
   if (wave == 0) {
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
   cx.s_c = s_c;
   cx.s_w = s_w;
   cx.s_slot = s_slot;
-  cx.lse_row = lse + tile * topk * 64 + x;
-  cx.want_lse = lse != nullptr;
+  cx.s_lse = s_lse;
+  cx.x = x;
   cx.lane = lane;
   cx.grp = grp;
   cx.col = col;
@@ -183,14 +186,15 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
   __syncthreads();
   const int n = uniform(s_n);
   cx.n = n;
-  if (lse && grp == 0)  // empty slots read lse = -inf
-    for (int i = 0; i < topk; ++i)
-      if (!((s_mask >> i) & 1)) cx.lse_row[i * 64] = -__builtin_huge_valf();
   if (n > 0) fwd_issue(cx, 0, k_lds[0], v_lds[0]);
   // unrolled by two: each step's buffers are fixed LDS addresses
   for (int u = 0; u < n; u += 2) {
     fwd_chunk(cx, u, bq, oacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
     if (u + 1 < n) fwd_chunk(cx, u + 1, bq, oacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+  }
+  if (lse) {
+    __syncthreads();
+    for (int e = tid; e < topk * 64; e += 256) lse[tile * topk * 64 + e] = s_lse[e];
   }
   // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
   bf16* orow = o + tile * 4096 + x * 64 + 4 * grp;
