@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GCA_ABI_VERSION 1
+#define GCA_ABI_VERSION 2
 
 typedef int gca_status;
 enum {
@@ -129,6 +129,33 @@ gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes);
 gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
                         const int32_t* q_pos, int32_t* idx, float* score, float* w,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gca_retrieve_gumbel -- gca_retrieve with Gumbel top-k selection (training).
+ *
+ * Definition: paperlayer.ai summary, section 3.2 (Training & Inference): while
+ * training, Gumbel noise is added to the relevance scores before the top-k
+ * selection, so that lower-scoring chunks keep a chance of being retrieved;
+ * section 5 credits Gumbel top-k sampling for pre-training up to 64K tokens.
+ *
+ * Same arguments, layouts, workspace (gca_workspace_size op 0) and errors as
+ * gca_retrieve, plus `seed`.  For every (g, b, h, t) and candidate j:
+ *   G_j = -ln(-ln U_j),  U_j = (m + 1/2) / 2^23,  m = top 23 bits of word
+ *   (j mod 4) of Philox4x32-10 (Salmon et al., SC 2011) with counter
+ *   (j / 4, t, (g*B + b)*H + h, 0) and key (seed mod 2^32, seed / 2^32);
+ *   the min(k, #candidates) best by (r_j + G_j descending, j ascending) are
+ *   selected (r_j + G_j formed as fma(dot, score_scale, G_j) in float32);
+ *   idx holds them in ascending j; score = the clean r_j of each selected
+ *   chunk (float32 dot product times score_scale) and w = Eq. 3 over those
+ *   clean scores, exactly as in gca_retrieve.  So gradients of w reach r, and
+ *   the noise only decides which chunks are kept.
+ * The same seed gives the same result on every call and for every workspace
+ * plan; the noise of a candidate does not depend on n_key or on other queries.
+ */
+gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void* lq,
+                               const void* lk, const int32_t* q_pos, int32_t* idx,
+                               float* score, float* w, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /*
  * gca_forward -- Eq. 2 per-chunk attention and Eq. 3 weighted fusion.

@@ -6,6 +6,7 @@ used for device memory and streams) and enqueue work on torch's current
 stream.  The entry points mirror the C ABI in include/gca.h:
 
   gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None)
+  gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None)
   gca_forward(shape, q, k, v, idx, w, o, lse=None)
   gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
                dlq=None, dlk=None, ws=None)
@@ -20,7 +21,7 @@ import os
 
 __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
-           "gca_workspace_size", "gca_retrieve", "gca_forward", "gca_backward", "OP_RETRIEVE",
+           "gca_workspace_size", "gca_retrieve", "gca_retrieve_gumbel", "gca_forward", "gca_backward", "OP_RETRIEVE",
            "OP_FORWARD", "OP_BACKWARD", "EXPORTED", "gca_num_kernels", "gca_kernel_name",
            "gca_timing_enable", "gca_timing_collect"]
 
@@ -28,7 +29,8 @@ GCA_F32 = 0
 GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
-            "gca_retrieve", "gca_forward", "gca_backward", "gca_num_kernels", "gca_kernel_name",
+            "gca_retrieve", "gca_retrieve_gumbel", "gca_forward", "gca_backward",
+            "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +87,8 @@ def load():
     lib.gca_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.gca_retrieve.restype = ctypes.c_int
     lib.gca_retrieve.argtypes = [sp] + [vp] * 6 + [vp, sz, vp]
+    lib.gca_retrieve_gumbel.restype = ctypes.c_int
+    lib.gca_retrieve_gumbel.argtypes = [sp, ctypes.c_uint64] + [vp] * 6 + [vp, sz, vp]
     lib.gca_forward.restype = ctypes.c_int
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
     lib.gca_backward.restype = ctypes.c_int
@@ -156,6 +160,15 @@ def gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None):
     _check(load().gca_retrieve(
         ctypes.byref(shape), _ptr(lq, "lq"), _ptr(lk, "lk"), _ptr(q_pos, "q_pos"),
         _ptr(idx, "idx"), _ptr(score, "score"), _ptr(w, "w"), _ptr(ws, "ws"),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None):
+    ws = _workspace(shape, OP_RETRIEVE, ws, lq)
+    _check(load().gca_retrieve_gumbel(
+        ctypes.byref(shape), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(lq, "lq"),
+        _ptr(lk, "lk"), _ptr(q_pos, "q_pos"), _ptr(idx, "idx"), _ptr(score, "score"),
+        _ptr(w, "w"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
 
 

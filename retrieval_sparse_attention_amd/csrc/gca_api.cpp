@@ -219,9 +219,10 @@ gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes) {
   return GCA_OK;
 }
 
-gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
-                        const int32_t* q_pos, int32_t* idx, float* score, float* w, void* ws,
-                        size_t ws_bytes, void* stream) {
+static gca_status retrieve_impl(const char* fn, const gca_shape* shape, int noise, uint64_t seed,
+                                const void* lq, const void* lk, const int32_t* q_pos,
+                                int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
+                                void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kRetrieve, &z));
   if (z.q_rows == 0) {
@@ -238,8 +239,8 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
   const RetrieveWs wl = retrieve_ws(shape, z, plan);
   if (wl.total > 0) {
     if (ws == nullptr || ws_bytes < wl.total)
-      return fail(GCA_ERR_WORKSPACE, "gca_retrieve needs %zu workspace bytes, got %zu",
-                  wl.total, ws == nullptr ? (size_t)0 : ws_bytes);
+      return fail(GCA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", fn, wl.total,
+                  ws == nullptr ? (size_t)0 : ws_bytes);
     if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
   }
   const int64_t nblk = shape->dtype == GCA_BF16
@@ -264,8 +265,24 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
   a.score = score;
   a.w = w;
   a.part = wl.total ? (uint64_t*)((char*)ws + wl.part) : nullptr;
+  a.noise = noise;
+  a.seed = seed;
   a.stream = (hipStream_t)stream;
-  return device_status(gca::launch_retrieve(plan, a), a.stream, "gca_retrieve");
+  return device_status(gca::launch_retrieve(plan, a), a.stream, fn);
+}
+
+gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
+                        const int32_t* q_pos, int32_t* idx, float* score, float* w, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return retrieve_impl("gca_retrieve", shape, 0, 0, lq, lk, q_pos, idx, score, w, ws, ws_bytes,
+                       stream);
+}
+
+gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void* lq,
+                               const void* lk, const int32_t* q_pos, int32_t* idx, float* score,
+                               float* w, void* ws, size_t ws_bytes, void* stream) {
+  return retrieve_impl("gca_retrieve_gumbel", shape, 1, seed, lq, lk, q_pos, idx, score, w, ws,
+                       ws_bytes, stream);
 }
 
 gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,

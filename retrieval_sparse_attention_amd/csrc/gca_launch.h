@@ -27,6 +27,8 @@ struct LaunchRetrieve {
   float* score;
   float* w;
   uint64_t* part;   // [heads * n_query * nsplit * kmax] candidate keys when nsplit > 1
+  int noise;        // 1: Gumbel top-k (selection on r + G), 0: plain top-k
+  uint64_t seed;    // Philox key of the Gumbel noise
   hipStream_t stream;
 };
 

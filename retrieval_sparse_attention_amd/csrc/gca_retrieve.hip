@@ -17,6 +17,15 @@
 //
 // f32 path.  One thread per query computes float32 dot products and keeps a
 // sorted register list; it serves the small float32 workloads.
+//
+// Gumbel top-k (paperlayer.ai summary, section 3.2: during training, Gumbel
+// noise is added to the relevance scores before the top-k selection).  Every
+// kernel here has a NOISE variant: candidate j of query q in linear head h is
+// ranked by r_j + G_j, with G_j = -ln(-ln U) and U = (m + 1/2) 2^-23 from the top
+// 23 bits m of word (j mod 4) of Philox4x32-10 (Salmon et al., SC 2011) at
+// counter (j / 4, q, h, 0) under the 64-bit seed.  The noise decides the
+// selection only: the reported scores and the fusion weights are computed from
+// the clean r of the selected chunks.
 
 #include "gca_device.h"
 #include "gca_launch.h"
@@ -109,6 +118,65 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): ten rounds, each
+// multiplying words 0 and 2 by the two round constants and recombining the
+// halves of the 64-bit products with words 1 and 3 and the key; the key steps
+// by the two Weyl increments between rounds.  The key is wave-uniform.
+struct Words4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
+    const uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return Words4{{c0, c1, c2, c3}};
+}
+
+// Standard Gumbel variate from one 32-bit word: U = (m + 1/2) 2^-23 (exact in
+// float32, strictly inside (0, 1)), E = -ln U taken through log1p above 1/2 so
+// that it keeps full relative accuracy near U = 1, G = -ln E.
+__device__ __forceinline__ float gumbel_from_word(uint32_t word) {
+  const float u = (float)(word >> 9) * 0x1p-23f + 0x1p-24f;
+  const float e = u <= 0.5f ? -logf(u) : -log1pf(u - 1.0f);
+  return -logf(e);
+}
+
+// Word e (0..3, any lane-varying value) without indexing a register array.
+__device__ __forceinline__ uint32_t word_at(const Words4& n, int e) {
+  return e == 0 ? n.w[0] : (e == 1 ? n.w[1] : (e == 2 ? n.w[2] : n.w[3]));
+}
+
+// Noise of candidates 4c .. 4c+3 of query q in linear head h.
+__device__ __forceinline__ Words4 gumbel_words(uint64_t seed, int64_t c, int64_t q, int64_t h) {
+  return philox4x32_10((uint32_t)c, (uint32_t)q, (uint32_t)h, 0u, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+// float32 dot product of two bf16 landmark rows (16-byte aligned, DL % 8 == 0),
+// in dimension order: the clean score of a selected candidate.
+__device__ __forceinline__ float dot_bf16_rows(const bf16* a, const bf16* b, int dl) {
+  float acc = 0.0f;
+  for (int d0 = 0; d0 < dl; d0 += 8) {
+    const bf16x8 x = *(const bf16x8*)(a + d0);
+    const bf16x8 y = *(const bf16x8*)(b + d0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+  }
+  return acc;
+}
+
 // Lower bound, in unscaled dot-product units, of every dot product a whose
 // score fl(a * scale) reaches t (inv_scale = 1 / scale, rounded): the relative
 // margin 2^-20 covers the three roundings involved and the absolute 1e-30
@@ -156,15 +224,25 @@ constexpr int kScanStride = kScanCap + 25;
 #endif
 constexpr int kScanPrefetch = GCA_SCAN_PREFETCH;  // landmark blocks in flight per wave
 
-// Bucket entries hold the raw dot product and the chunk index of a candidate;
-// the selection key (which needs the scaled score) is formed only here.
+// Bucket entries hold the raw dot product (with noise: the perturbed score
+// itself) and the chunk index of a candidate; the selection key is formed only
+// here.
 struct ScanEntry {
   float raw;
   int j;
 };
 
+template <bool NOISE>
 __device__ __forceinline__ uint64_t entry_key(ScanEntry e, float score_scale) {
+  if (NOISE) return make_key(e.raw + 0.0f, e.j);
   return make_key(e.raw * score_scale + 0.0f, e.j);  // +0.0f: -0 scores compare as +0
+}
+
+// The threshold in the units the scan compares: raw dot products without
+// noise (a bound through raw_bound), the perturbed score itself with noise.
+template <bool NOISE>
+__device__ __forceinline__ float tau_from_score(float t, float inv_scale) {
+  return NOISE ? t : raw_bound(t, inv_scale);
 }
 
 // Exact top k of every query's kept list plus its bucket (256 threads: 8 per
@@ -179,7 +257,7 @@ __device__ __forceinline__ uint64_t entry_key(ScanEntry e, float score_scale) {
 //     below k give the sorted top k.
 // Kept out of line: the scan loop that calls it then has no inner loops, and
 // the compiler keeps precise load-wait counts across its iterations.
-template <int KMAX>
+template <int KMAX, bool NOISE>
 __device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX],
                                                        int* cnt, int* nkept, int* ncnt,
                                                        float* tau_raw, int k, float score_scale,
@@ -203,7 +281,7 @@ __device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64
     if (p < per) {
       const int i = sub + 8 * p;
       const ScanEntry v = b[i];
-      e[p] = i < n ? entry_key(v, score_scale) : 0;
+      e[p] = i < n ? entry_key<NOISE>(v, score_scale) : 0;
     }
   }
 #pragma unroll
@@ -262,17 +340,19 @@ __device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64
   if (sub == 0) {
     cnt[q] = 0;
     nkept[q] = m;
-    tau_raw[q] = m == k ? raw_bound(key_score(kept[q][k - 1]), inv_scale) : -__builtin_huge_valf();
+    tau_raw[q] = m == k ? tau_from_score<NOISE>(key_score(kept[q][k - 1]), inv_scale)
+                        : -__builtin_huge_valf();
   }
   __syncthreads();
 }
 
-template <int DL, int KMAX>
+template <int DL, int KMAX, bool NOISE>
 __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
     const bf16* __restrict__ lq, const bf16* __restrict__ lk, const int32_t* __restrict__ q_pos,
     int64_t n_query, int64_t n_key, int n_qtiles, int nsplit, int64_t split_len,
     float score_scale, int k, int softmax_one, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out, float* __restrict__ w_out, uint64_t* __restrict__ part) {
+    float* __restrict__ score_out, float* __restrict__ w_out, uint64_t* __restrict__ part,
+    uint64_t seed) {
   constexpr int NKS = DL / 16;  // MFMA K-steps over the landmark dimension
   constexpr int HALF = DL / 2;  // landmark dims supplied by each lane half
   constexpr int PF = kScanPrefetch;
@@ -360,6 +440,17 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) acc = mfma32x32x16(ring[s][ks], bq[ks], acc);
       load_block(blk + 128 * PF, ring[s]);
+      if (NOISE) {
+        // perturbed scores fl(r * scale + G): rows 8g + 4 half + e (e = 0..3)
+        // are four consecutive candidates, one Philox call
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const Words4 nz = gumbel_words(seed, (blk + 4 * half + 8 * g4) >> 2, q, head);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[4 * g4 + e] = fmaf(acc[4 * g4 + e], score_scale, gumbel_from_word(nz.w[e]));
+        }
+      }
       // candidate blk + c_row(r, half) is eligible iff c_row(r, half) - 4*half < rem
       const int64_t rem64 = lim - blk - 4 * half;
       const int rem = rem64 < 0 ? 0 : (rem64 > 32 ? 32 : (int)rem64);
@@ -378,9 +469,10 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         const uint32_t fb = first_bound[col];
         const float b_raw = (fb & 0x80000000u) ? __uint_as_float(fb ^ 0x80000000u)
                                                : __uint_as_float(~fb);
-        // the scores of the offered candidates reach fl(b_raw * scale); the
-        // bound stays valid for every later round
-        tl = fmaxf(tl, raw_bound(b_raw * score_scale + 0.0f, inv_scale));
+        // the scores of the offered candidates reach fl(b_raw * scale) (with
+        // noise: b_raw is the perturbed score); the bound stays valid for
+        // every later round
+        tl = fmaxf(tl, NOISE ? b_raw : raw_bound(b_raw * score_scale + 0.0f, inv_scale));
         if (tid < 32) tau_raw[tid] = tl;  // lane tid < 32 holds query col = tid
       }
       int nh = 0;
@@ -429,10 +521,11 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
       }
       __syncthreads();
       if (round + 1 < n_rounds && full[round % 3])
-        scan_compact<KMAX>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
+        scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
+                                  inv_scale);
     }
   }
-  scan_compact<KMAX>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
+  scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
 
   const int qs = tid >> 3, sub = tid & 7;
   const int64_t qq = (int64_t)qt * 32 + qs;
@@ -440,10 +533,31 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   const int m = nkept[qs];
   const int64_t qrow = head * n_query + qq;
   if (nsplit == 1) {
+    float clean[KMAX];
+    if (NOISE) {
+      // clean scores of the selected candidates: thread sub computes entries
+      // sub and sub + 8, then the 8 threads of the query share them
+      const bf16* lq_row = lq + qrow * DL;
+      const bf16* lk_h = lk + head * n_key * DL;
+      float c0 = 0.0f, c1 = 0.0f;
+      if (sub < m)
+        c0 = dot_bf16_rows(lq_row, lk_h + (int64_t)key_index(kept[qs][sub]) * DL, DL) *
+             score_scale;
+      if (KMAX > 8 && sub + 8 < m)
+        c1 = dot_bf16_rows(lq_row, lk_h + (int64_t)key_index(kept[qs][sub + 8]) * DL, DL) *
+             score_scale;
+      const int base = lane & ~7;
+#pragma unroll
+      for (int p = 0; p < KMAX; ++p) clean[p] = __shfl(p < 8 ? c0 : c1, base + (p & 7));
+    }
     if (sub == 0) {
       float s[KMAX];
       int id[KMAX];
       keys_to_list<KMAX>(kept[qs], m, s, id);
+      if (NOISE) {
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) s[p] = p < m ? clean[p] : -__builtin_huge_valf();
+      }
       finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                            w_out + qrow * k);
     }
@@ -461,14 +575,18 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
 // ---------------------------------------------------------------------------
 constexpr int kMergeMax = 4096;  // nsplit * KMAX limit (LDS list size)
 
-template <int KMAX>
+template <int KMAX, bool NOISE>
 __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ part, int n,
                                                    int k, int softmax_one,
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ score_out,
-                                                   float* __restrict__ w_out) {
+                                                   float* __restrict__ w_out,
+                                                   const bf16* __restrict__ lq,
+                                                   const bf16* __restrict__ lk, int64_t n_query,
+                                                   int64_t n_key, int dl, float score_scale) {
   __shared__ uint64_t lst[kMergeMax];
   __shared__ uint64_t out[KMAX];
+  __shared__ float clean[KMAX];  // with noise: clean scores of the selected
   const int lane = threadIdx.x;
   const int64_t qrow = blockIdx.x;
   const uint64_t* src = part + qrow * n;
@@ -528,10 +646,24 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
     if (r < k) out[r] = me;
   }
   __syncthreads();
+  const int m = n2 < k ? n2 : k;
+  if (NOISE) {
+    if (lane < m) {
+      const int64_t head = qrow / n_query;
+      clean[lane] = dot_bf16_rows(lq + qrow * dl,
+                                  lk + (head * n_key + key_index(out[lane])) * dl, dl) *
+                    score_scale;
+    }
+    __syncthreads();
+  }
   if (lane == 0) {
     float s[KMAX];
     int id[KMAX];
-    keys_to_list<KMAX>(out, n2 < k ? n2 : k, s, id);
+    keys_to_list<KMAX>(out, m, s, id);
+    if (NOISE) {
+#pragma unroll
+      for (int p = 0; p < KMAX; ++p) s[p] = p < m ? clean[p] : -__builtin_huge_valf();
+    }
     finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                          w_out + qrow * k);
   }
@@ -540,12 +672,12 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // float32 scan: one thread per (head, query).
 // ---------------------------------------------------------------------------
-template <int KMAX>
+template <int KMAX, bool NOISE>
 __global__ __launch_bounds__(64) void k_scan_topk_f32(
     const float* __restrict__ lq, const float* __restrict__ lk, const int32_t* __restrict__ q_pos,
     int64_t n_heads, int64_t n_query, int64_t n_key, int dl, float score_scale, int k,
     int softmax_one, int32_t* __restrict__ idx_out, float* __restrict__ score_out,
-    float* __restrict__ w_out) {
+    float* __restrict__ w_out, uint64_t seed) {
   const int64_t qrow = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (qrow >= n_heads * n_query) return;
   const int64_t head = qrow / n_query, q = qrow % n_query;
@@ -560,8 +692,23 @@ __global__ __launch_bounds__(64) void k_scan_topk_f32(
   for (int64_t j = 0; j < n_cand; ++j) {
     float acc = 0.0f;
     for (int d = 0; d < dl; ++d) acc = fmaf(lqr[d], lkh[j * dl + d], acc);
-    const float x = acc * score_scale;
+    float x = acc * score_scale;
+    if (NOISE) {
+      const Words4 nz = gumbel_words(seed, j >> 2, q, head);
+      x = fmaf(acc, score_scale, gumbel_from_word(word_at(nz, (int)(j & 3))));
+    }
     if (better(x, (int)j, s[KMAX - 1], id[KMAX - 1])) list_insert(s, id, x, (int)j);
+  }
+  if (NOISE) {
+    // clean scores of the selected: the same dot products, recomputed in the
+    // same order
+#pragma unroll
+    for (int p = 0; p < KMAX; ++p) {
+      if (id[p] == kIdxNone) continue;
+      float acc = 0.0f;
+      for (int d = 0; d < dl; ++d) acc = fmaf(lqr[d], lkh[(int64_t)id[p] * dl + d], acc);
+      s[p] = acc * score_scale;
+    }
   }
   finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                        w_out + qrow * k);
@@ -570,7 +717,7 @@ __global__ __launch_bounds__(64) void k_scan_topk_f32(
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <int KMAX>
+template <int KMAX, bool NOISE>
 static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
   const int64_t heads = a.G * a.B * a.H;
   if (a.dtype == 1) {
@@ -578,37 +725,44 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
     {
     KernelTimer timer(kKernScan, a.stream);
     if (a.dl == 64)
-      hipLaunchKernelGGL((k_scan_topk_bf16<64, KMAX>), dim3((unsigned)nblk), dim3(256), 0,
+      hipLaunchKernelGGL((k_scan_topk_bf16<64, KMAX, NOISE>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,
-                         a.softmax_one, a.idx, a.score, a.w, a.part);
+                         a.softmax_one, a.idx, a.score, a.w, a.part, a.seed);
     else
-      hipLaunchKernelGGL((k_scan_topk_bf16<32, KMAX>), dim3((unsigned)nblk), dim3(256), 0,
+      hipLaunchKernelGGL((k_scan_topk_bf16<32, KMAX, NOISE>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,
-                         a.softmax_one, a.idx, a.score, a.w, a.part);
+                         a.softmax_one, a.idx, a.score, a.w, a.part, a.seed);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t rows = heads * a.n_query;
     KernelTimer timer(kKernMerge, a.stream);
-    hipLaunchKernelGGL((k_topk_merge<KMAX>), dim3((unsigned)rows), dim3(64), 0, a.stream, a.part,
-                       pl.nsplit * KMAX, a.k, a.softmax_one, a.idx, a.score, a.w);
+    hipLaunchKernelGGL((k_topk_merge<KMAX, NOISE>), dim3((unsigned)rows), dim3(64), 0, a.stream,
+                       a.part, pl.nsplit * KMAX, a.k, a.softmax_one, a.idx, a.score, a.w,
+                       (const bf16*)a.lq, (const bf16*)a.lk, a.n_query, a.n_key, a.dl,
+                       a.score_scale);
     return hipGetLastError();
   }
   const int64_t rows = heads * a.n_query;
   KernelTimer timer(kKernScan, a.stream);
-  hipLaunchKernelGGL((k_scan_topk_f32<KMAX>), dim3((unsigned)((rows + 63) / 64)), dim3(64), 0,
-                     a.stream, (const float*)a.lq, (const float*)a.lk, a.q_pos, heads,
+  hipLaunchKernelGGL((k_scan_topk_f32<KMAX, NOISE>), dim3((unsigned)((rows + 63) / 64)), dim3(64),
+                     0, a.stream, (const float*)a.lq, (const float*)a.lk, a.q_pos, heads,
                      a.n_query, a.n_key, a.dl, a.score_scale, a.k, a.softmax_one, a.idx,
-                     a.score, a.w);
+                     a.score, a.w, a.seed);
   return hipGetLastError();
 }
 
+template <int KMAX>
+static hipError_t launch_scan_n(const ScanPlan& pl, const LaunchRetrieve& a) {
+  return a.noise ? launch_scan_k<KMAX, true>(pl, a) : launch_scan_k<KMAX, false>(pl, a);
+}
+
 hipError_t launch_retrieve(const ScanPlan& pl, const LaunchRetrieve& a) {
-  if (pl.kmax == 4) return launch_scan_k<4>(pl, a);
-  if (pl.kmax == 8) return launch_scan_k<8>(pl, a);
-  return launch_scan_k<16>(pl, a);
+  if (pl.kmax == 4) return launch_scan_n<4>(pl, a);
+  if (pl.kmax == 8) return launch_scan_n<8>(pl, a);
+  return launch_scan_n<16>(pl, a);
 }
 
 }  // namespace gca

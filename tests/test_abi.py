@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert gca.gca_abi_version() == 1
+    assert gca.gca_abi_version() == 2
     assert gca.gca_status_string(0) == "GCA_OK"
     assert gca.gca_status_string(3) == "GCA_ERR_WORKSPACE"
     assert gca.gca_status_string(99) == "GCA_UNKNOWN_STATUS"

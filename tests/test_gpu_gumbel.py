@@ -1,0 +1,167 @@
+"""GPU parity of gca_retrieve_gumbel (Gumbel top-k) against the float64 oracle.
+
+The selection is decided by perturbed scores r + G that the GPU forms in
+float32 and the oracle in float64.  Where the oracle's k-th and (k+1)-th
+perturbed scores are at least GAP apart the selection is unique and the GPU's
+indices must equal the oracle's exactly.  GAP is far above the float32 error of
+r + G (the dot product's accumulation and the two logarithms of the noise stay
+below 1e-5 here).  Inside GAP several selections are correct: the GPU's must
+hold every candidate clearly above the cut, none clearly below it, and such
+queries must stay rare.  Scores and weights are compared for the GPU's own
+selection, computed by the oracle from the clean scores.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import retrieval_sparse_attention_amd as gca
+import synth
+from oracle import gca_oracle as orc
+from oracle import gumbel as gb
+from gpu_common import close, dev, f64, require_gpu, shape_of
+
+pytestmark = pytest.mark.gpu
+
+GAP = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_gumbel(shape, seed, lq, lk, q_pos):
+    G, B, H, Nq, k = shape.G, shape.B, shape.H, shape.n_query, shape.top_k
+    idx = torch.full((G, B, H, Nq, k), -7, dtype=torch.int32, device="cuda")
+    score = torch.full((G, B, H, Nq, k), float("nan"), dtype=torch.float32, device="cuda")
+    w = torch.full((G, B, H, Nq, k), float("nan"), dtype=torch.float32, device="cuda")
+    gca.gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), f64(score), f64(w)
+
+
+def check_gumbel(lq, lk, q_pos, k, score_scale, softmax_one, seed, got, is_bf16):
+    """Compares one Gumbel retrieval with the oracle; returns (#unique, #ambiguous)."""
+    idx, score, w = got
+    lq64, lk64 = f64(lq), f64(lk)
+    G, B, H, Nq, _ = lq64.shape
+    ref_score = np.zeros_like(score)
+    ref_w = np.zeros_like(w)
+    unique = ambiguous = 0
+    for g in range(G):
+        for b in range(B):
+            for h in range(H):
+                head = (g * B + b) * H + h
+                for q in range(Nq):
+                    r, p = gb.perturbed_scores(lq64[g, b, h, q], lk64[g, b, h], q_pos[q],
+                                               score_scale, seed, head, q)
+                    n = r.shape[0]
+                    m = min(k, n)
+                    row = idx[g, b, h, q]
+                    assert np.all(row[m:] == -1), (g, b, h, q, row)
+                    sel = row[:m].astype(np.int64)
+                    assert np.all(np.diff(sel) > 0), (g, b, h, q, row)
+                    assert np.all((sel >= 0) & (sel < n)), (g, b, h, q, row)
+                    if m == 0:
+                        continue
+                    if m == n:
+                        assert np.array_equal(sel, np.arange(n))
+                        unique += 1
+                    else:
+                        order = np.lexsort((np.arange(n), -p))
+                        kth, nxt = p[order[m - 1]], p[order[m]]
+                        if kth - nxt >= GAP:
+                            assert np.array_equal(sel, np.sort(order[:m])), (g, b, h, q)
+                            unique += 1
+                        else:
+                            ambiguous += 1
+                            assert np.all(p[sel] >= kth - GAP), (g, b, h, q)
+                            must = np.flatnonzero(p > kth + GAP)
+                            assert np.all(np.isin(must, sel)), (g, b, h, q)
+                    ref_score[g, b, h, q, :m] = r[sel]
+                    ref_w[g, b, h, q, :m] = orc.fusion_weights(r[sel], softmax_one)
+    close("score", score, ref_score, is_bf16)
+    close("w", w, ref_w, is_bf16)
+    assert ambiguous <= max(2, (unique + ambiguous) // 100), (unique, ambiguous)
+    return unique, ambiguous
+
+
+def _training_case(name, seed, **over):
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, with_dout=False, **over)
+    shape = shape_of(cfg)
+    got = run_gumbel(shape, seed, dev(x["lq"]), dev(x["lk"]), dev(x["q_pos"]))
+    check_gumbel(x["lq"], x["lk"], x["q_pos"].numpy(), cfg["k"], cfg["score_scale"],
+                 cfg["softmax_one"], seed, got, cfg["dtype"] == "bf16")
+    return cfg, x, got
+
+
+def test_gumbel_tiny_fp32():
+    _training_case("tiny_fp32", seed=11)
+
+
+def test_gumbel_fp32_ragged_k3():
+    _training_case("tiny_fp32", seed=12, n_query=21, n_key=21, S=5, D=7, Dl=9, k=3, H=3,
+                   softmax_one=1)
+
+
+@pytest.mark.parametrize("k", [1, 5, 8, 16])
+def test_gumbel_bf16_small(k):
+    # 72 query chunks: two full 32-query tiles plus a ragged tail of 8
+    _training_case("train16k_fwdbwd_g2", seed=100 + k, B=2, H=2, n_query=72, n_key=72, k=k)
+
+
+def test_gumbel_bf16_landmark_dim_32():
+    _training_case("train16k_fwd", seed=5, B=1, H=3, n_query=40, n_key=40, Dl=32)
+
+
+def test_gumbel_bf16_training_full_size():
+    # the 16K-token training step of two groups: 24576 queries, noise on every candidate
+    cfg, x, got = _training_case("train16k_fwdbwd_g2", seed=2024)
+    # the noise changes the selection of many queries
+    clean = orc.retrieve(f64(x["lq"][:, :1, :2]), f64(x["lk"][:, :1, :2]), x["q_pos"].numpy(),
+                         cfg["k"], cfg["score_scale"], cfg["softmax_one"])[0]
+    assert np.mean(np.any(got[0][:, :1, :2] != clean, axis=-1)) > 0.5
+
+
+def _sliced_inputs(n_query, n_key, dl, seed):
+    g = torch.Generator().manual_seed(seed)
+    lq = (torch.randn(1, 1, 3, n_query, dl, generator=g) * 0.125).to(torch.bfloat16)
+    lk = (torch.randn(1, 1, 3, n_key, dl, generator=g) * 0.125).to(torch.bfloat16)
+    return lq, lk
+
+
+@pytest.mark.parametrize("k,dl", [(1, 64), (8, 64), (16, 64), (8, 32)])
+def test_gumbel_bf16_sliced_scan_and_merge(k, dl):
+    # 6000 candidates: the scan is cut into slices and a merge kernel finishes;
+    # query positions cover full, partial and tiny candidate sets
+    n_query, n_key = 40, 6000
+    lq, lk = _sliced_inputs(n_query, n_key, dl, seed=k * 7 + dl)
+    q_pos = torch.tensor([n_key + 1] * 30 + [4000, 2500, 1025, 1024, 700, 129, 128, 9, 2, 0],
+                         dtype=torch.int32)
+    shape = gca.make_shape(1, 1, 3, n_query, n_key, 64, 64, dl, k, gca.GCA_BF16, 0)
+    assert gca.gca_workspace_size(shape, gca.OP_RETRIEVE) > 0  # sliced plan
+    seed = 0x1234_5678_9ABC_DEF0 + k
+    got = run_gumbel(shape, seed, dev(lq), dev(lk), dev(q_pos))
+    check_gumbel(lq, lk, q_pos.numpy(), k, shape.score_scale, 0, seed, got, True)
+
+
+def test_gumbel_is_deterministic_and_plan_independent():
+    n_query, dl, k = 24, 64, 8
+    lq, lk = _sliced_inputs(n_query, 3000, dl, seed=3)
+    q_pos = torch.tensor([1000 - 3 * i for i in range(n_query)], dtype=torch.int32)
+    seed = 77
+    sliced = gca.make_shape(1, 1, 3, n_query, 3000, 64, 64, dl, k, gca.GCA_BF16, 1)
+    single = gca.make_shape(1, 1, 3, n_query, 1000, 64, 64, dl, k, gca.GCA_BF16, 1)
+    assert gca.gca_workspace_size(sliced, gca.OP_RETRIEVE) > 0
+    assert gca.gca_workspace_size(single, gca.OP_RETRIEVE) == 0
+    a = run_gumbel(sliced, seed, dev(lq), dev(lk), dev(q_pos))
+    b = run_gumbel(sliced, seed, dev(lq), dev(lk), dev(q_pos))
+    c = run_gumbel(single, seed, dev(lq), dev(lk[:, :, :, :1000]), dev(q_pos))
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y)  # same call twice: same bits
+        assert np.array_equal(x, z)  # slices + merge == one pass over the first 1000
+    other = run_gumbel(sliced, seed + 1, dev(lq), dev(lk), dev(q_pos))
+    assert not np.array_equal(other[0], a[0])
+    check_gumbel(lq, lk, q_pos.numpy(), k, sliced.score_scale, 1, seed, a, True)
