@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the 16M-token retrieval and 1M-token inference measurements")
     ap.add_argument("--infer-steps", type=int, default=1000)
+    ap.add_argument("--no-gumbel", action="store_true",
+                    help="skip the training step with Gumbel top-k retrieval")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, one device-to-device copy of BYTES "
@@ -156,6 +158,31 @@ def _timed(fn, reps):
     gca.gca_timing_enable(False)
     per = {k: v[0] / v[1] for k, v in gca.gca_timing_collect().items() if v[1]}
     return e0.elapsed_time(e1) / reps, per
+
+
+def bench_gumbel_step(shape, d, bufs, steps):
+    """The same training step with gca_retrieve_gumbel (a fresh seed per step,
+    as in training) in place of gca_retrieve."""
+    import retrieval_sparse_attention_amd as gca
+    idx, score, w, o, lse, dq, dk, dv, dw, dscore, dlq, dlk, wsr, wsb = bufs
+    seed = [1000]
+
+    def step():
+        seed[0] += 1
+        gca.gca_retrieve_gumbel(shape, seed[0], d["lq"], d["lk"], d["q_pos"], idx, score, w,
+                                ws=wsr)
+        gca.gca_forward(shape, d["q"], d["k"], d["v"], idx, w, o, lse)
+        gca.gca_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"],
+                         dq, dk, dv, dw, dscore, dlq, dlk, ws=wsb)
+
+    for _ in range(3):
+        step()
+    ms, per = _timed(step, steps)
+    tokens = shape.B * shape.n_query * shape.chunk_size
+    return {"retrieval": "gca_retrieve_gumbel (Philox4x32-10 Gumbel noise, new seed per step)",
+            "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 4), "steps": steps,
+            "scan_us": round(per.get("scan_topk", 0.0) * 1e3, 2)}
 
 
 def bench_retrieve16m(reps=20):
@@ -361,6 +388,13 @@ def main():
         print(f"[bench] copy reference: {n} bytes read, {n} bytes written", file=sys.stderr,
               flush=True)
         del src, dst
+    gumbel = None
+    if not args.no_gumbel:
+        bufs = (idx, score, w, o, lse, dq, dk, dv, dw, dscore, dlq, dlk, wsr, wsb)
+        gumbel = bench_gumbel_step(shape, d, bufs, args.steps)
+        gumbel["scan_us_without_noise"] = kernels.get("scan_topk", {}).get("avg_us")
+        print(f"[bench] Gumbel top-k training step: {gumbel['ms_per_step']} ms",
+              file=sys.stderr, flush=True)
     long_ctx = {}
     if not args.no_long_context:
         long_ctx["retrieve16m"] = bench_retrieve16m()
@@ -393,6 +427,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "long_context": long_ctx or None,
+        "gumbel_train_step": gumbel,
         "wall_s_timed": round(wall, 3),
         "source_digest": digest,
     }
