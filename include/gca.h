@@ -158,6 +158,36 @@ gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void
                                void* stream);
 
 /*
+ * gca_gather_kv -- packs the retrieved K/V tiles, for K/V kept in host memory.
+ *
+ * Definition: paperlayer.ai summary, section 3.2 (past chunk representations
+ * may be offloaded to CPU memory; the transfers retrieval needs happen only
+ * when it runs); paperhub.cn review page, authors' reply "Q2" (the offloaded
+ * GCA K/V is shared within a group; a host link above 20 GB/s suffices).
+ *
+ * For every (g, b, h, t) and slot i with c = idx[g,b,h,t,i]:
+ *   c in [0, n_key):  k_packed[g,b,h, t*k + i] = k[g,b,h,c] (one S x D tile),
+ *                     v_packed likewise, idx_packed[g,b,h,t,i] = t*k + i
+ *   otherwise:        zero tiles and idx_packed = -1.
+ * gca_forward / gca_backward over (k_packed, v_packed, idx_packed) with a shape
+ * whose n_key is n_query * top_k give the same results as over (k, v, idx):
+ * only k tiles per query chunk cross the host link instead of the whole K/V.
+ *
+ *   shape           G, B, H, n_query, n_key, chunk_size, head_dim, top_k, dtype
+ *                   (the same limits as gca_forward)
+ *   idx        [G, B, H, Nq, k]          int32, device memory
+ *   k, v       [G, B, H, Nk, S, D]       dtype, big; device memory OR pinned host
+ *                                        memory (hipHostMalloc); other host memory
+ *                                        is refused with GCA_ERR_INVALID_ARGUMENT
+ *   k_packed, v_packed [G, B, H, Nq*k, S, D]  dtype, big, device, output
+ *   idx_packed [G, B, H, Nq, k]          int32, device, output
+ * The whole [G, B, H, Nk, S, D] range of k and v must lie in one allocation.
+ */
+gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void* k,
+                         const void* v, void* k_packed, void* v_packed, int32_t* idx_packed,
+                         void* stream);
+
+/*
  * gca_forward -- Eq. 2 per-chunk attention and Eq. 3 weighted fusion.
  *
  * Definition: long-context-modeling README, "Model Architecture" (first stage:

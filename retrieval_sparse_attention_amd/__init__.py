@@ -7,6 +7,7 @@ stream.  The entry points mirror the C ABI in include/gca.h:
 
   gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None)
   gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None)
+  gca_gather_kv(shape, idx, k, v, k_packed, v_packed, idx_packed)   k, v may be pinned host
   gca_forward(shape, q, k, v, idx, w, o, lse=None)
   gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
                dlq=None, dlk=None, ws=None)
@@ -21,15 +22,16 @@ import os
 
 __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
-           "gca_workspace_size", "gca_retrieve", "gca_retrieve_gumbel", "gca_forward", "gca_backward", "OP_RETRIEVE",
-           "OP_FORWARD", "OP_BACKWARD", "EXPORTED", "gca_num_kernels", "gca_kernel_name",
-           "gca_timing_enable", "gca_timing_collect"]
+           "gca_workspace_size", "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv",
+           "gca_forward", "gca_backward", "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
+           "EXPORTED", "gca_num_kernels", "gca_kernel_name", "gca_timing_enable",
+           "gca_timing_collect"]
 
 GCA_F32 = 0
 GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
-            "gca_retrieve", "gca_retrieve_gumbel", "gca_forward", "gca_backward",
+            "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv", "gca_forward", "gca_backward",
             "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect")
 
@@ -89,6 +91,8 @@ def load():
     lib.gca_retrieve.argtypes = [sp] + [vp] * 6 + [vp, sz, vp]
     lib.gca_retrieve_gumbel.restype = ctypes.c_int
     lib.gca_retrieve_gumbel.argtypes = [sp, ctypes.c_uint64] + [vp] * 6 + [vp, sz, vp]
+    lib.gca_gather_kv.restype = ctypes.c_int
+    lib.gca_gather_kv.argtypes = [sp] + [vp] * 6 + [vp]
     lib.gca_forward.restype = ctypes.c_int
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
     lib.gca_backward.restype = ctypes.c_int
@@ -170,6 +174,24 @@ def gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None):
         _ptr(lk, "lk"), _ptr(q_pos, "q_pos"), _ptr(idx, "idx"), _ptr(score, "score"),
         _ptr(w, "w"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def _ptr_readable(t, name):
+    """Address of a contiguous device tensor or pinned host tensor."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gca_gather_kv(shape, idx, k, v, k_packed, v_packed, idx_packed):
+    _check(load().gca_gather_kv(
+        ctypes.byref(shape), _ptr(idx, "idx"), _ptr_readable(k, "k"), _ptr_readable(v, "v"),
+        _ptr(k_packed, "k_packed"), _ptr(v_packed, "v_packed"), _ptr(idx_packed, "idx_packed"),
+        _stream()))
 
 
 def gca_forward(shape, q, k, v, idx, w, o, lse=None):

@@ -179,6 +179,29 @@ gca_status opt(const void* p, const char* name, size_t align) {
   return GCA_OK;
 }
 
+// Device-side address of a buffer the GPU may read: device or managed memory
+// as is; pinned host memory through the address its mapping has on the
+// device.  Unregistered host memory is refused: a kernel reading it would
+// fault.
+gca_status readable_on_device(const void* p, const char* name, const void** dev) {
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess || at.type == hipMemoryTypeUnregistered) {
+    (void)hipGetLastError();  // clear the sticky error of the query
+    return fail(GCA_ERR_INVALID_ARGUMENT,
+                "%s is neither device memory nor pinned (hipHostMalloc) host memory", name);
+  }
+  if (at.type == hipMemoryTypeHost) {
+    if (at.devicePointer == nullptr)
+      return fail(GCA_ERR_INVALID_ARGUMENT, "%s: host memory without a device mapping", name);
+    const char* base = at.hostPointer ? (const char*)at.hostPointer : (const char*)p;
+    *dev = (const char*)at.devicePointer + ((const char*)p - base);
+  } else {
+    *dev = p;
+  }
+  return GCA_OK;
+}
+
 #define GCA_TRY(expr)                 \
   do {                                \
     gca_status st_ = (expr);          \
@@ -283,6 +306,42 @@ gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void
                                float* w, void* ws, size_t ws_bytes, void* stream) {
   return retrieve_impl("gca_retrieve_gumbel", shape, 1, seed, lq, lk, q_pos, idx, score, w, ws,
                        ws_bytes, stream);
+}
+
+gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void* k,
+                         const void* v, void* k_packed, void* v_packed, int32_t* idx_packed,
+                         void* stream) {
+  Sizes z;
+  GCA_TRY(check_shape(shape, kForward, &z));
+  if (z.slots == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  if (z.slots > 0x7fffffffLL)
+    return fail(GCA_ERR_UNSUPPORTED, "G*B*H*n_query*top_k must be below 2^31");
+  GCA_TRY(need(idx, "idx", 4));
+  GCA_TRY(need(k_packed, "k_packed", 16));
+  GCA_TRY(need(v_packed, "v_packed", 16));
+  GCA_TRY(need(idx_packed, "idx_packed", 4));
+  gca::LaunchGather a{};
+  if (shape->n_key > 0) {
+    GCA_TRY(need(k, "k", 16));
+    GCA_TRY(need(v, "v", 16));
+    GCA_TRY(readable_on_device(k, "k", &a.k_src));
+    GCA_TRY(readable_on_device(v, "v", &a.v_src));
+  }
+  a.heads = z.heads;
+  a.n_query = shape->n_query;
+  a.n_key = shape->n_key;
+  a.k = shape->top_k;
+  a.tile_bytes = (int64_t)shape->chunk_size * shape->head_dim *
+                 (shape->dtype == GCA_BF16 ? 2 : 4);
+  a.idx = idx;
+  a.k_out = k_packed;
+  a.v_out = v_packed;
+  a.idx_out = idx_packed;
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_gather_kv(a), a.stream, "gca_gather_kv");
 }
 
 gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,

@@ -72,6 +72,19 @@ struct LaunchBackward {
   hipStream_t stream;
 };
 
+struct LaunchGather {
+  int64_t heads, n_query, n_key;
+  int k;
+  int64_t tile_bytes;    // S * D * element size
+  const void* k_src;     // device address of k (device memory or mapped host memory)
+  const void* v_src;
+  const int32_t* idx;
+  void* k_out;           // [heads, n_query * k, S, D]
+  void* v_out;
+  int32_t* idx_out;      // [heads, n_query, k]
+  hipStream_t stream;
+};
+
 // Kernels the library launches, for the event timing facility.
 enum KernelId {
   kKernScan = 0,
@@ -80,7 +93,8 @@ enum KernelId {
   kKernReverseIndex = 3,
   kKernBackwardQ = 4,
   kKernBackwardKV = 5,
-  kNumKernels = 6
+  kKernGather = 6,
+  kNumKernels = 7
 };
 
 // Records a HIP event pair around one kernel launch on `stream` when timing is
@@ -101,5 +115,6 @@ class KernelTimer {
 hipError_t launch_retrieve(const ScanPlan& plan, const LaunchRetrieve& a);
 hipError_t launch_forward(const LaunchForward& a);
 hipError_t launch_backward(const LaunchBackward& a);
+hipError_t launch_gather_kv(const LaunchGather& a);
 
 }  // namespace gca

@@ -42,7 +42,8 @@ hipEvent_t take_event(TimingState& s) {
 }
 
 const char* kNames[kNumKernels] = {"scan_topk", "topk_merge", "forward",
-                                   "reverse_index", "backward_q", "backward_kv"};
+                                   "reverse_index", "backward_q", "backward_kv",
+                                   "gather_kv"};
 
 }  // namespace
 

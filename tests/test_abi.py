@@ -125,3 +125,18 @@ def test_empty_problem_is_a_no_op():
     s = _bf16_shape(n_query=0, n_key=0)
     assert _status("gca_forward", ctypes.byref(s), None, None, None, None, None, None, None,
                    None)[0] == 0
+
+
+def test_gather_rejects_before_any_device_call():
+    s = _bf16_shape()
+    st, msg = _status("gca_gather_kv", ctypes.byref(s), None, A, A, A, A, A, None)
+    assert st == 1 and "idx is NULL" in msg
+    st, msg = _status("gca_gather_kv", ctypes.byref(s), A, A, A, MIS, A, A, None)
+    assert st == 1 and "k_packed" in msg and "aligned" in msg
+    st, msg = _status("gca_gather_kv", ctypes.byref(s), A, None, A, A, A, A, None)
+    assert st == 1 and "k is NULL" in msg
+    bad = _bf16_shape(chunk_size=32)
+    assert _status("gca_gather_kv", ctypes.byref(bad), A, A, A, A, A, A, None)[0] == 2
+    empty = _bf16_shape(n_query=0)
+    assert _status("gca_gather_kv", ctypes.byref(empty), None, None, None, None, None, None,
+                   None)[0] == 0
