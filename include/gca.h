@@ -188,6 +188,43 @@ gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void*
                          void* stream);
 
 /*
+ * Sliding-window self-attention -- the other attention of a DRT layer.
+ *
+ * Definition: paperlayer.ai summary, section 1 and section 3.2 (every layer
+ * pairs GCA with fixed-size sliding-window self-attention, keeping the cost
+ * linear in the sequence) and section 4.1.2 (a 512-token window).  Token x of
+ * a (b, h) sequence attends to the keys y with x - window < y <= x:
+ *   O[x] = sum_y P[x,y] V[y],  P[x,.] = softmax_y(scale <Q[x], K[y]>),
+ *   lse[x] = log sum_y exp(scale <Q[x], K[y]>)                (float32)
+ * Backward, with D[x] = <dO[x], O[x]> (O as written by the forward):
+ *   dS = P (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+ *
+ *   q, k, v, o, dout, dq, dk, dv   [B, H, T, head_dim]   bf16, big
+ *   lse                            [B, H, T]             float32
+ * Supported: dtype GCA_BF16, head_dim 64, T a multiple of 64 (whole 64-token
+ * chunks), window >= 1 (any value; windows >= T give causal attention),
+ * B*H*T/64 < 2^31.  Same conventions, checks and errors as the GCA calls.
+ * gca_swa_backward needs a workspace of gca_swa_workspace_size bytes (D rows).
+ */
+typedef struct {
+  int64_t B, H, T;  /* batch, heads, tokens per sequence */
+  int32_t head_dim; /* D */
+  int32_t window;   /* W */
+  gca_dtype dtype;
+  float scale;      /* usually 1/sqrt(head_dim) */
+} gca_swa_shape;
+
+gca_status gca_swa_workspace_size(const gca_swa_shape* shape, size_t* bytes);
+
+gca_status gca_swa_forward(const gca_swa_shape* shape, const void* q, const void* k,
+                           const void* v, void* o, float* lse /* or NULL */, void* stream);
+
+gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
  * gca_forward -- Eq. 2 per-chunk attention and Eq. 3 weighted fusion.
  *
  * Definition: long-context-modeling README, "Model Architecture" (first stage:

@@ -26,7 +26,8 @@ Arrays: q, k, v, o, dout [B, H, T, D]; lse [B, H, T].
 
 import numpy as np
 
-__all__ = ["window_mask", "swa_forward", "swa_backward"]
+__all__ = ["window_mask", "swa_forward", "swa_backward", "swa_query_rows",
+           "swa_key_rows"]
 
 
 def window_mask(T, window):
@@ -84,3 +85,56 @@ def swa_backward(q, k, v, dout, window, scale):
             dq[b, h] = float(scale) * (ds @ k[b, h])
             dk[b, h] = float(scale) * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def _row(q, k, v, x, window, scale):
+    """P row, O row and LSE of query x of one head (keys max(0, x-W+1) .. x)."""
+    lo = max(0, x - int(window) + 1)
+    s = float(scale) * (k[lo:x + 1] @ q[x])
+    m = s.max()
+    l = m + np.log(np.exp(s - m).sum())
+    p = np.exp(s - l)
+    return lo, p, p @ v[lo:x + 1], l
+
+
+def swa_query_rows(q, k, v, dout, window, scale, b, h, xs):
+    """For the listed query rows x of head (b, h): O[x], LSE[x] and dQ[x],
+    each computed from that row's own window alone (for spot checks of
+    long sequences)."""
+    q = np.asarray(q[b, h], dtype=np.float64)
+    k = np.asarray(k[b, h], dtype=np.float64)
+    v = np.asarray(v[b, h], dtype=np.float64)
+    do = None if dout is None else np.asarray(dout[b, h], dtype=np.float64)
+    o_rows, lse_rows, dq_rows = [], [], []
+    for x in xs:
+        lo, p, o_x, l = _row(q, k, v, x, window, scale)
+        o_rows.append(o_x)
+        lse_rows.append(l)
+        if do is not None:
+            dp = v[lo:x + 1] @ do[x]
+            ds = p * (dp - do[x] @ o_x)
+            dq_rows.append(float(scale) * (ds @ k[lo:x + 1]))
+    return np.array(o_rows), np.array(lse_rows), (np.array(dq_rows) if do is not None else None)
+
+
+def swa_key_rows(q, k, v, dout, window, scale, b, h, ys):
+    """dK[y] and dV[y] of head (b, h) for the listed key rows y, summed over the
+    queries x in [y, y + W - 1] that see them."""
+    q = np.asarray(q[b, h], dtype=np.float64)
+    k = np.asarray(k[b, h], dtype=np.float64)
+    v = np.asarray(v[b, h], dtype=np.float64)
+    do = np.asarray(dout[b, h], dtype=np.float64)
+    T = q.shape[0]
+    dk_rows, dv_rows = [], []
+    for y in ys:
+        dk_y = np.zeros(q.shape[1])
+        dv_y = np.zeros(v.shape[1])
+        for x in range(y, min(T, y + int(window))):
+            lo, p, o_x, _ = _row(q, k, v, x, window, scale)
+            p_xy = p[y - lo]
+            dv_y += p_xy * do[x]
+            ds_xy = p_xy * (v[y] @ do[x] - do[x] @ o_x)
+            dk_y += float(scale) * ds_xy * q[x]
+        dk_rows.append(dk_y)
+        dv_rows.append(dv_y)
+    return np.array(dk_rows), np.array(dv_rows)

@@ -12,6 +12,9 @@ stream.  The entry points mirror the C ABI in include/gca.h:
   gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
                dlq=None, dlk=None, ws=None)
   gca_workspace_size(shape, op)          op: 0 retrieve, 1 forward, 2 backward
+  gca_swa_forward(swa_shape, q, k, v, o, lse=None)      sliding-window self-attention
+  gca_swa_backward(swa_shape, q, k, v, o, lse, dout, dq, dk, dv, ws=None)
+  gca_swa_workspace_size(swa_shape)
 
 A missing library raises; there is no fallback path.
 """
@@ -23,7 +26,9 @@ import os
 __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
            "gca_workspace_size", "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv",
-           "gca_forward", "gca_backward", "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
+           "gca_forward", "gca_backward", "GcaSwaShape", "make_swa_shape",
+           "gca_swa_workspace_size", "gca_swa_forward", "gca_swa_backward",
+           "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
            "EXPORTED", "gca_num_kernels", "gca_kernel_name", "gca_timing_enable",
            "gca_timing_collect"]
 
@@ -33,7 +38,8 @@ OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
             "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv", "gca_forward", "gca_backward",
             "gca_num_kernels", "gca_kernel_name",
-            "gca_timing_enable", "gca_timing_collect")
+            "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
+            "gca_swa_forward", "gca_swa_backward")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -45,6 +51,17 @@ class GcaShape(ctypes.Structure):
                 ("landmark_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("softmax_one", ctypes.c_int32),
                 ("attn_scale", ctypes.c_float), ("score_scale", ctypes.c_float)]
+
+
+class GcaSwaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def make_swa_shape(B, H, T, head_dim, window, dtype=GCA_BF16, scale=None):
+    return GcaSwaShape(B, H, T, head_dim, window, dtype,
+                       1.0 / math.sqrt(head_dim) if scale is None else scale)
 
 
 class GcaError(RuntimeError):
@@ -97,6 +114,13 @@ def load():
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
     lib.gca_backward.restype = ctypes.c_int
     lib.gca_backward.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
+    swp = ctypes.POINTER(GcaSwaShape)
+    lib.gca_swa_workspace_size.restype = ctypes.c_int
+    lib.gca_swa_workspace_size.argtypes = [swp, ctypes.POINTER(sz)]
+    lib.gca_swa_forward.restype = ctypes.c_int
+    lib.gca_swa_forward.argtypes = [swp] + [vp] * 5 + [vp]
+    lib.gca_swa_backward.restype = ctypes.c_int
+    lib.gca_swa_backward.argtypes = [swp] + [vp] * 10 + [sz, vp]
     lib.gca_num_kernels.restype = ctypes.c_int
     lib.gca_num_kernels.argtypes = []
     lib.gca_kernel_name.restype = ctypes.c_char_p
@@ -209,6 +233,31 @@ def gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dsco
         _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"), _ptr(dw, "dw"), _ptr(dscore, "dscore"),
         _ptr(dlq, "dlq"), _ptr(dlk, "dlk"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_swa_workspace_size(shape):
+    n = ctypes.c_size_t(0)
+    _check(load().gca_swa_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gca_swa_forward(shape, q, k, v, o, lse=None):
+    _check(load().gca_swa_forward(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(o, "o"),
+        _ptr(lse, "lse"), _stream()))
+
+
+def gca_swa_backward(shape, q, k, v, o, lse, dout, dq, dk, dv, ws=None):
+    if ws is None:
+        n = gca_swa_workspace_size(shape)
+        if n:
+            import torch
+            ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(load().gca_swa_backward(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(o, "o"),
+        _ptr(lse, "lse"), _ptr(dout, "dout"), _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"),
+        _ptr(ws, "ws"), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+        _stream()))
 
 
 def gca_num_kernels():

@@ -344,6 +344,104 @@ gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void*
   return device_status(gca::launch_gather_kv(a), a.stream, "gca_gather_kv");
 }
 
+static gca_status check_swa(const gca_swa_shape* s, int64_t* heads) {
+  if (s == nullptr) return fail(GCA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->T < 0)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T >= 0");
+  if (s->window < 1) return fail(GCA_ERR_INVALID_ARGUMENT, "window must be >= 1");
+  if (s->dtype != GCA_F32 && s->dtype != GCA_BF16)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "dtype must be GCA_F32 or GCA_BF16");
+  if (!std::isfinite(s->scale)) return fail(GCA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (s->dtype != GCA_BF16 || s->head_dim != 64)
+    return fail(GCA_ERR_UNSUPPORTED, "sliding-window attention needs bf16 and head_dim 64");
+  if (s->T % 64 != 0) return fail(GCA_ERR_UNSUPPORTED, "T must be a multiple of 64");
+  int64_t h, rows;
+  if (!mul_ok(s->B, s->H, &h) || !mul_ok(h, s->T, &rows) || rows > (int64_t(1) << 40))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "tensor sizes overflow");
+  if (rows / 64 > 0x7fffffffLL) return fail(GCA_ERR_UNSUPPORTED, "more than 2^31 - 1 blocks");
+  *heads = h;
+  return GCA_OK;
+}
+
+gca_status gca_swa_workspace_size(const gca_swa_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return fail(GCA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  int64_t heads;
+  GCA_TRY(check_swa(shape, &heads));
+  *bytes = align_up((size_t)heads * (size_t)shape->T * sizeof(float));
+  g_err[0] = '\0';
+  return GCA_OK;
+}
+
+gca_status gca_swa_forward(const gca_swa_shape* shape, const void* q, const void* k,
+                           const void* v, void* o, float* lse, void* stream) {
+  int64_t heads;
+  GCA_TRY(check_swa(shape, &heads));
+  if (shape->T == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  GCA_TRY(need(q, "q", 16));
+  GCA_TRY(need(k, "k", 16));
+  GCA_TRY(need(v, "v", 16));
+  GCA_TRY(need(o, "o", 16));
+  GCA_TRY(opt(lse, "lse", 4));
+  gca::LaunchSwa a{};
+  a.heads = heads;
+  a.n_tok = shape->T;
+  a.window = shape->window;
+  a.scale = shape->scale;
+  a.q = q;
+  a.kk = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_swa_forward(a), a.stream, "gca_swa_forward");
+}
+
+gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const void* k,
+                            const void* v, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                            void* stream) {
+  int64_t heads;
+  GCA_TRY(check_swa(shape, &heads));
+  if (shape->T == 0) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
+  GCA_TRY(need(q, "q", 16));
+  GCA_TRY(need(k, "k", 16));
+  GCA_TRY(need(v, "v", 16));
+  GCA_TRY(need(o, "o", 16));
+  GCA_TRY(need(lse, "lse", 4));
+  GCA_TRY(need(dout, "dout", 16));
+  GCA_TRY(need(dq, "dq", 16));
+  GCA_TRY(need(dk, "dk", 16));
+  GCA_TRY(need(dv, "dv", 16));
+  const size_t wsz = align_up((size_t)heads * (size_t)shape->T * sizeof(float));
+  if (ws == nullptr || ws_bytes < wsz)
+    return fail(GCA_ERR_WORKSPACE, "gca_swa_backward needs %zu workspace bytes, got %zu", wsz,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
+  gca::LaunchSwa a{};
+  a.heads = heads;
+  a.n_tok = shape->T;
+  a.window = shape->window;
+  a.scale = shape->scale;
+  a.q = q;
+  a.kk = k;
+  a.v = v;
+  a.o = o;
+  a.lse = (float*)lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)ws;
+  a.stream = (hipStream_t)stream;
+  return device_status(gca::launch_swa_backward(a), a.stream, "gca_swa_backward");
+}
+
 gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,
                        const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
   Sizes z;

@@ -85,6 +85,23 @@ struct LaunchGather {
   hipStream_t stream;
 };
 
+struct LaunchSwa {
+  int64_t heads, n_tok;  // B * H, T (a multiple of 64)
+  int window;
+  float scale;
+  const void* q;
+  const void* kk;
+  const void* v;
+  const void* o;         // backward: the forward's output
+  float* lse;            // [heads, T]; written by the forward (may be NULL), read by the backward
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;          // workspace [heads, T]: <dO[x], O[x]>
+  hipStream_t stream;
+};
+
 // Kernels the library launches, for the event timing facility.
 enum KernelId {
   kKernScan = 0,
@@ -94,7 +111,10 @@ enum KernelId {
   kKernBackwardQ = 4,
   kKernBackwardKV = 5,
   kKernGather = 6,
-  kNumKernels = 7
+  kKernSwaForward = 7,
+  kKernSwaBackwardQ = 8,
+  kKernSwaBackwardKV = 9,
+  kNumKernels = 10
 };
 
 // Records a HIP event pair around one kernel launch on `stream` when timing is
@@ -116,5 +136,7 @@ hipError_t launch_retrieve(const ScanPlan& plan, const LaunchRetrieve& a);
 hipError_t launch_forward(const LaunchForward& a);
 hipError_t launch_backward(const LaunchBackward& a);
 hipError_t launch_gather_kv(const LaunchGather& a);
+hipError_t launch_swa_forward(const LaunchSwa& a);
+hipError_t launch_swa_backward(const LaunchSwa& a);
 
 }  // namespace gca

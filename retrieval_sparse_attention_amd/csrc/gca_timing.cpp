@@ -43,7 +43,8 @@ hipEvent_t take_event(TimingState& s) {
 
 const char* kNames[kNumKernels] = {"scan_topk", "topk_merge", "forward",
                                    "reverse_index", "backward_q", "backward_kv",
-                                   "gather_kv"};
+                                   "gather_kv", "swa_forward", "swa_backward_q",
+                                   "swa_backward_kv"};
 
 }  // namespace
 

@@ -24,7 +24,7 @@ import numpy as np
 import torch
 
 __all__ = ["WORKLOADS", "workload", "training_inputs", "context_landmarks",
-           "device_kv", "query_batch", "kv_tiles_host"]
+           "device_kv", "query_batch", "kv_tiles_host", "SWA_WORKLOADS", "swa_inputs"]
 
 # Sizes of each workload, named by what it is.
 WORKLOADS = {
@@ -260,3 +260,28 @@ def query_batch(name, lk, step=0, seed=None, accept=None, accept_heads=None, lk6
                         todo = todo[~ok]
     q_pos = torch.full((Nq,), q_pos_val, dtype=torch.int32)
     return dict(q=q, lq=lq, q_pos=q_pos, needle=torch.from_numpy(needle), cfg=cfg)
+
+
+# Sliding-window self-attention of the same layer: the 16K-token training batch
+# (B=4, H=12, 16384 tokens, head dim 64) with the pages' 512-token window.
+SWA_WORKLOADS = {
+    "train16k_swa": dict(B=4, H=12, T=16384, D=64, window=512, seed=6),
+}
+
+
+def swa_inputs(B, H, T, D, seed, device="cpu"):
+    """q, k, v, dout [B, H, T, D] bf16, N(0, 1) each (so that scale * <q, k> has
+    unit spread at scale 1/sqrt(D)).  Large sizes are drawn on `device` with a
+    seeded torch generator, one tensor at a time; small ones (device "cpu")
+    from numpy's PCG64 sub-streams q, k, v, dout."""
+    if device == "cpu":
+        rs = _streams(seed)
+        return {name: _normal(rs[name], (B, H, T, D), 1.0, "bf16")
+                for name in ("q", "k", "v", "dout")}
+    g = torch.Generator(device=device)
+    out = {}
+    for i, name in enumerate(("q", "k", "v", "dout")):
+        g.manual_seed(seed * 16 + i)
+        out[name] = torch.randn((B, H, T, D), generator=g, device=device,
+                                dtype=torch.float32).to(torch.bfloat16)
+    return out

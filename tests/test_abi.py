@@ -140,3 +140,21 @@ def test_gather_rejects_before_any_device_call():
     empty = _bf16_shape(n_query=0)
     assert _status("gca_gather_kv", ctypes.byref(empty), None, None, None, None, None, None,
                    None)[0] == 0
+
+
+def test_swa_checks_before_any_device_call():
+    ok = gca.make_swa_shape(2, 3, 1024, 64, 512)
+    assert gca.gca_swa_workspace_size(ok) == ((2 * 3 * 1024 * 4 + 255) // 256) * 256
+    n = ctypes.c_size_t(0)
+    for bad, code in ((gca.make_swa_shape(1, 1, 100, 64, 512), 2),
+                      (gca.make_swa_shape(1, 1, 128, 32, 512), 2),
+                      (gca.make_swa_shape(1, 1, 128, 64, 512, dtype=gca.GCA_F32), 2),
+                      (gca.make_swa_shape(1, 1, 128, 64, 0), 1),
+                      (gca.make_swa_shape(0, 1, 128, 64, 8), 1)):
+        st, msg = _status("gca_swa_workspace_size", ctypes.byref(bad), ctypes.byref(n))
+        assert st == code and msg
+    st, msg = _status("gca_swa_forward", ctypes.byref(ok), A, A, None, A, None, None)
+    assert st == 1 and "v is NULL" in msg
+    st, msg = _status("gca_swa_backward", ctypes.byref(ok), A, A, A, A, A, A, A, A, A, A,
+                      ctypes.c_size_t(16), None)
+    assert st == 3 and "workspace" in msg

@@ -96,3 +96,18 @@ def test_finite_differences():
             args[which][pos] -= 2 * h
             dn = loss(*args)
             assert abs((up - dn) / (2 * h) - grad[pos]) < 1e-7, (which, pos)
+
+
+def test_row_helpers_match_the_full_computation():
+    q, k, v, do = _inputs(2, 2, 30, 4, 6)
+    W, sc = 7, 0.4
+    o, lse = swa.swa_forward(q, k, v, W, sc)
+    dq, dk, dv = swa.swa_backward(q, k, v, do, W, sc)
+    xs = [0, 1, 6, 7, 29]
+    o_r, l_r, dq_r = swa.swa_query_rows(q, k, v, do, W, sc, 1, 0, xs)
+    assert np.allclose(o_r, o[1, 0, xs], rtol=0, atol=1e-13)
+    assert np.allclose(l_r, lse[1, 0, xs], rtol=0, atol=1e-13)
+    assert np.allclose(dq_r, dq[1, 0, xs], rtol=0, atol=1e-13)
+    dk_r, dv_r = swa.swa_key_rows(q, k, v, do, W, sc, 0, 1, xs)
+    assert np.allclose(dk_r, dk[0, 1, xs], rtol=0, atol=1e-13)
+    assert np.allclose(dv_r, dv[0, 1, xs], rtol=0, atol=1e-13)
