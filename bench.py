@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the 16M-token retrieval and 1M-token inference measurements")
     ap.add_argument("--infer-steps", type=int, default=1000)
+    ap.add_argument("--no-swa", action="store_true",
+                    help="skip the sliding-window self-attention step")
     ap.add_argument("--no-gumbel", action="store_true",
                     help="skip the training step with Gumbel top-k retrieval")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -183,6 +185,57 @@ def bench_gumbel_step(shape, d, bufs, steps):
             "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
             "ms_per_step": round(ms, 4), "steps": steps,
             "scan_us": round(per.get("scan_topk", 0.0) * 1e3, 2)}
+
+
+def swa_pairs(T, W):
+    """(query, key) pairs inside a causal window of W over T tokens."""
+    W = min(W, T)
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def bench_swa(steps):
+    """Sliding-window self-attention of the same layer over the 16K-token
+    batch (B=4, H=12, T=16384, D=64, W=512): forward + backward per step."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+    cfg = synth.SWA_WORKLOADS["train16k_swa"]
+    B, H, T, D, W = cfg["B"], cfg["H"], cfg["T"], cfg["D"], cfg["window"]
+    x = synth.swa_inputs(B, H, T, D, cfg["seed"], device="cuda")
+    shape = gca.make_swa_shape(B, H, T, D, W)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+    ws = torch.empty(gca.gca_swa_workspace_size(shape), dtype=torch.uint8, device="cuda")
+
+    def step():
+        gca.gca_swa_forward(shape, x["q"], x["k"], x["v"], o, lse)
+        gca.gca_swa_backward(shape, x["q"], x["k"], x["v"], o, lse, x["dout"], dq, dk, dv, ws=ws)
+
+    for _ in range(3):
+        step()
+    ms, per = _timed(step, steps)
+    pairs = B * H * swa_pairs(T, W)
+    # algorithmic flops over the pairs inside the window: 2 products (QK, PV)
+    # forward, 5 (QK, dO V^T, dQ, dK, dV) backward, 2*D flops each
+    work = {"swa_forward": 2 * 2 * D * pairs, "swa_backward_q": 3 * 2 * D * pairs,
+            "swa_backward_kv": 4 * 2 * D * pairs}
+    kern = {}
+    for name, f in work.items():
+        t = per.get(name)
+        if t:
+            tf = f / (t * 1e-3) / 1e12
+            kern[name] = dict(avg_us=round(t * 1e3, 2), tflops=round(tf, 1),
+                              frac=round(tf / (MFMA_BF16_PEAK / 1e12), 4))
+    tokens = B * T
+    return {"workload": "train16k_swa", "B": B, "H": H, "tokens": T, "head_dim": D,
+            "window": W, "step": "gca_swa_forward + gca_swa_backward", "steps": steps,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "pairs": pairs, "kernels": kern,
+            "algorithmic_flops_per_step": 2 * D * pairs * (2 + 5),
+            "note": "backward recomputes S and dP in both kernels (7 tile products per "
+                    "pair instead of 5); flops above count the 5 the math needs"}
 
 
 def bench_retrieve16m(reps=20):
@@ -476,6 +529,11 @@ def main():
         print(f"[bench] copy reference: {n} bytes read, {n} bytes written", file=sys.stderr,
               flush=True)
         del src, dst
+    swa_res = None
+    if not args.no_swa:
+        swa_res = bench_swa(args.steps)
+        print(f"[bench] sliding-window attention step: {swa_res['ms_per_step']} ms",
+              file=sys.stderr, flush=True)
     gumbel = None
     if not args.no_gumbel:
         bufs = (idx, score, w, o, lse, dq, dk, dv, dw, dscore, dlq, dlk, wsr, wsb)
@@ -520,6 +578,7 @@ def main():
         "kernels": kernels,
         "long_context": long_ctx or None,
         "gumbel_train_step": gumbel,
+        "sliding_window_step": swa_res,
         "wall_s_timed": round(wall, 3),
         "source_digest": digest,
     }
