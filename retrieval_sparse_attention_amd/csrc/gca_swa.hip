@@ -15,8 +15,9 @@
 // the diagonal tile and the tile where the window starts need masks.
 //   k_swa_fwd_bf16    : one 4-wave workgroup per query block; each wave owns 16
 //                       query rows; K/V tiles stream into double-buffered LDS
-//                       (asynchronous copies) and an online softmax (running
-//                       max and sum per row) carries O across tiles.
+//                       (asynchronous copies) and an online softmax carries O
+//                       across tiles (offset raised only when the row max grows
+//                       by more than 2^8; the row sum formed on MFMA).
 //   k_swa_bwd_q_bf16  : one workgroup per query block; D from dO and O, then
 //                       dQ over the block's key tiles; writes D.
 //   k_swa_bwd_kv_bf16 : one workgroup per key block; dK, dV over the query
@@ -57,9 +58,17 @@ __device__ __forceinline__ void swa_fwd_issue(const SwaFwdCtx& cx, int u, bf16* 
   cx.dma->copy_async(vd, cx.v_head + j * 4096);
 }
 
-// Key tile u of the block (buffers kt/vt); the next tile goes to kn/vn.
+// Offset growth (log2 units) tolerated before O and the row sum are rescaled:
+// probabilities stay below 2^8 in the meantime, far inside float32 and bf16
+// range, and O and the sum always share one offset, so the result is exact.
+constexpr float kRescaleSlack = 8.0f;
+
+// Key tile u of the block (buffers kt/vt); the next tile goes to kn/vn.  mb is
+// the row's exponent offset in log2 units (starts at -1e30: no key yet), lacc
+// the row sum of the bf16 probabilities, formed on MFMA with an all-ones
+// operand so that it matches the probabilities that multiply V.
 __device__ __forceinline__ void swa_fwd_tile(const SwaFwdCtx& cx, int u, const bf16x8 (&bq)[2],
-                                             f32x4 (&oacc)[4], float& m_run, float& l_run,
+                                             f32x4 (&oacc)[4], f32x4& lacc, float& mb,
                                              const bf16* __restrict__ kt,
                                              const bf16* __restrict__ vt, bf16* __restrict__ kn,
                                              bf16* __restrict__ vn) {
@@ -96,29 +105,26 @@ __device__ __forceinline__ void swa_fwd_tile(const SwaFwdCtx& cx, int u, const b
   for (int r = 1; r < 4; ++r)
     m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
   m = xor32_max(xor16_max(m));
-  const float m_new = fmaxf(m_run, m);
-  // a row with no key in the window yet keeps m = -inf: use 0 as its offset
-  const float mb = (m_new == -__builtin_huge_valf() ? 0.0f : m_new) * cx.c2;
-  const float alpha = fast_exp2(fmaf(m_run, cx.c2, -mb));
-  float lp[4];
+  const float mt2 = m * cx.c2;  // -inf while the row has no key in the window
+  if (__any(mt2 > mb + kRescaleSlack)) {
+    const float mb_new = mt2 > mb + kRescaleSlack ? mt2 : mb;
+    const float alpha = fast_exp2(mb - mb_new);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    lp[mt] = 0.0f;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
-      sacc[mt][r] = e;
-      lp[mt] += e;
-    }
+      for (int e = 0; e < 4; ++e) oacc[dt][e] *= alpha;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lacc[e] *= alpha;
+    mb = mb_new;
   }
-  const float l = xor32_sum(xor16_sum((lp[0] + lp[1]) + (lp[2] + lp[3])));
-  l_run = fmaf(l_run, alpha, l);
-  m_run = m_new;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) oacc[dt][e] *= alpha;
-  // O^T (d x x) += V^T (d x j) P^T (j x x), P not yet normalised
+    for (int r = 0; r < 4; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
+  // O^T (d x x) += V^T (d x j) P^T (j x x) and the row sum 1^T P^T, P unnormalised
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     bf16x8 bp;
@@ -129,6 +135,7 @@ __device__ __forceinline__ void swa_fwd_tile(const SwaFwdCtx& cx, int u, const b
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma16x16x32(va[kb][dt], bp, oacc[dt]);
+    lacc = mfma16x16x32(ones, bp, lacc);
   }
 }
 
@@ -156,7 +163,8 @@ __global__ __launch_bounds__(256) void k_swa_fwd_bf16(const bf16* __restrict__ q
     for (int kd = 0; kd < 2; ++kd) bq[kd] = *(const bf16x8*)(row + 32 * kd);
   }
   f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  float m_run = -__builtin_huge_valf(), l_run = 0.0f;
+  f32x4 lacc = zero4();
+  float mb = -1e30f;
   const TileDma<4> dma(wave, lane);
   SwaFwdCtx cx;
   cx.dma = &dma;
@@ -174,11 +182,12 @@ __global__ __launch_bounds__(256) void k_swa_fwd_bf16(const bf16* __restrict__ q
   const int n = cx.n;
   swa_fwd_issue(cx, 0, k_lds[0], v_lds[0]);
   for (int u = 0; u < n; u += 2) {
-    swa_fwd_tile(cx, u, bq, oacc, m_run, l_run, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
+    swa_fwd_tile(cx, u, bq, oacc, lacc, mb, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
     if (u + 1 < n)
-      swa_fwd_tile(cx, u + 1, bq, oacc, m_run, l_run, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+      swa_fwd_tile(cx, u + 1, bq, oacc, lacc, mb, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
   }
-  // every row sees at least its own key: l_run > 0
+  // every row sees at least its own key: l > 0
+  const float l_run = lacc[0];
   const float inv_l = fast_rcp(l_run);
   bf16* orow = o + tile * 4096 + x * 64 + 4 * grp;
 #pragma unroll
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(256) void k_swa_fwd_bf16(const bf16* __restrict__ q
     for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[dt][e] * inv_l);
     *(bf16x4*)(orow + 16 * dt) = val;
   }
-  if (lse && grp == 0) lse[tile * 64 + x] = scale * m_run + fast_ln(l_run);
+  if (lse && grp == 0) lse[tile * 64 + x] = mb * 0.69314718055994531f + fast_ln(l_run);
 }
 
 // ---------------------------------------------------------------------------
