@@ -17,13 +17,13 @@
 //   2. S^T = K Q^T on MFMA (A = K rows from LDS, B = Q^T kept in registers), so a
 //      lane holds 16 of the 64 logits of ONE query row and the lanes l ^ 16,
 //      l ^ 32, l ^ 48 the others: the row max and row sum need two exchanges;
-//   3. p = exp2((s - max) * attn_scale * log2 e), l = sum p,
-//      L = attn_scale * max + ln l;
-//   4. the fusion weight is folded into the probabilities, p * (w_i / l), which
-//      become the B operand of O^T += V^T P^T directly from the S^T registers,
-//      so all k slots accumulate into ONE float32 accumulator; V^T comes from
-//      LDS through the gfx950 transpose read.  Each chunk's softmax is
-//      complete inside one 64-key tile: no running rescale is needed.
+//   3. p = exp2((s - max) * attn_scale * log2 e), rounded to bf16 once;
+//   4. V^T P^T (V^T from LDS through the gfx950 transpose read) and the row
+//      sums l = 1^T P^T are both MFMA products of the same bf16 p, so the
+//      softmax's sum costs no vector adds; L = attn_scale * max + ln l;
+//   5. O^T += (w_i / l) V^T P^T: all k slots accumulate into ONE float32
+//      accumulator.  Each chunk's softmax is complete inside one 64-key tile:
+//      no running rescale is needed.
 // O is rounded to bf16 once at the end.
 //
 // f32 path.  One thread per query row, float32 throughout (small workloads).
@@ -91,35 +91,38 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
     m = max_nc(m, max_nc(max_nc(sacc[0][r], sacc[1][r]), max_nc(sacc[2][r], sacc[3][r])));
   m = xor32_max(xor16_max(m));
   const float mb = m * cx.c2;
-  float lp[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    lp[mt] = 0.0f;
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
-      sacc[mt][r] = e;
-      lp[mt] += e;
-    }
-  }
-  const float l = xor32_sum(xor16_sum((lp[0] + lp[1]) + (lp[2] + lp[3])));
-  if (grp == 0) cx.s_lse[uniform(cx.s_slot[u]) * 64 + cx.x] = cx.attn_scale * m + fast_ln(l);
-  const float ps = cx.s_w[u] * fast_rcp(l);
-
-  // O^T (d x x) += V^T (d x j) * P^T (j x x).  K-step kb covers keys
-  // 32kb + 4*grp + 0..3 (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile
-  // 2kb+1): exactly what this lane holds; V^T comes by transpose reads.
+    for (int r = 0; r < 4; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
+  // V^T P^T (d x x) of this chunk and its row sums 1^T P^T, both on MFMA from
+  // the same bf16 probabilities; K-step kb covers keys 32kb + 4*grp + 0..3
+  // (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile 2kb+1): exactly what
+  // this lane holds; V^T comes by transpose reads.
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+  f32x4 pv[4], lacc = zero4();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     bf16x8 bp;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bp[e] = (bf16)(sacc[2 * kb][e] * ps);
-      bp[4 + e] = (bf16)(sacc[2 * kb + 1][e] * ps);
+      bp[e] = (bf16)sacc[2 * kb][e];
+      bp[4 + e] = (bf16)sacc[2 * kb + 1][e];
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = mfma16x16x32(va[kb][dt], bp, oacc[dt]);
+    for (int dt = 0; dt < 4; ++dt) pv[dt] = mfma16x16x32(va[kb][dt], bp, kb ? pv[dt] : zero4());
+    lacc = mfma16x16x32(ones, bp, lacc);
   }
+  const float l = lacc[0];
+  if (grp == 0) cx.s_lse[uniform(cx.s_slot[u]) * 64 + cx.x] = cx.attn_scale * m + fast_ln(l);
+  // O^T += (w_i / l) V^T P^T: the fusion weight and the normalisation in one factor
+  const float ps = cx.s_w[u] * fast_rcp(l);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(ps, pv[dt][e], oacc[dt][e]);
 }
 
 __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
