@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the 16M-token retrieval and 1M-token inference measurements")
     ap.add_argument("--infer-steps", type=int, default=1000)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cold-cache step, the copy rate and the one-group forward")
     ap.add_argument("--no-swa", action="store_true",
                     help="skip the sliding-window self-attention step")
     ap.add_argument("--no-gumbel", action="store_true",
@@ -238,6 +240,81 @@ def bench_swa(steps):
                     "pair instead of 5); flops above count the 5 the math needs"}
 
 
+def bench_train16k_fwd(steps):
+    """The 16K-token forward of one group (G=1, vanilla weights, aliased landmarks):
+    gca_retrieve + gca_forward per step, against max(HBM, MFMA) time of the forward's
+    algorithmic bytes and flops."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+    name = "train16k_fwd"
+    cfg = synth.workload(name)
+    x = synth.training_inputs(name, with_dout=False)
+    d = {key: val.contiguous().cuda() for key, val in x.items() if key != "cfg"}
+    G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
+    S, D, Dl, k = cfg["S"], cfg["D"], cfg["Dl"], cfg["k"]
+    shape = gca.make_shape(G, B, H, Nq, Nk, S, D, Dl, k, gca.GCA_BF16, cfg["softmax_one"])
+    idx = torch.empty((G, B, H, Nq, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((G, B, H, Nq, k), device="cuda")
+    w = torch.empty_like(score)
+    o = torch.empty_like(d["q"])
+    lse = torch.empty((G, B, H, Nq, k, S), device="cuda")
+
+    def step():
+        gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], idx, score, w)
+        gca.gca_forward(shape, d["q"], d["k"], d["v"], idx, w, o, lse)
+
+    for _ in range(3):
+        step()
+    ms, per = _timed(step, steps)
+    pairs = int((idx >= 0).sum().item())
+    wk = kernel_work(cfg, pairs)["forward"]
+    fwd_s = per.get("forward", 0.0) * 1e-3
+    t_roof = max(wk["bytes"] / HBM_PEAK, wk["flops"] / MFMA_BF16_PEAK)
+    return {"workload": name, "G": G, "B": B, "H": H, "tokens": Nq * S, "pairs": pairs,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * Nq * S / (ms / 1e3), 1),
+            "forward_us": round(fwd_s * 1e6, 2), "scan_us": round(per.get("scan_topk", 0.0) * 1e3, 2),
+            "forward_GBps": round(wk["bytes"] / fwd_s / 1e9, 1) if fwd_s else None,
+            "forward_TFLOPs": round(wk["flops"] / fwd_s / 1e12, 1) if fwd_s else None,
+            "forward_roofline_us": round(t_roof * 1e6, 2),
+            "forward_roofline_frac": round(t_roof / fwd_s, 4) if fwd_s else None}
+
+
+def bench_cold_and_copy(step, reps=5):
+    """The training step "cold": a 512 MB buffer is written before each timed step so that
+    the last-level cache (MALL) holds none of the inputs; plus the rate of a plain 1 GiB
+    device-to-device copy, the HBM rate a streaming kernel reaches on this machine."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cold = []
+    for r in range(reps):
+        flush.fill_(float(r))
+        torch.cuda.synchronize()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    src = torch.ones(2**30 // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 5 / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"cold_ms_per_step_median": round(float(np.median(cold)), 4), "cold_reps": reps,
+            "copy_1GiB_read_plus_write_GBps": round(2 * 2**30 / copy_s / 1e9, 1)}
+
+
 def bench_retrieve16m(reps=20):
     """16,777,216-token resident context (262144 chunks of 64, K/V ~51.5 GB):
     32 query chunks retrieve top-8 from every chunk, then attend and fuse."""
@@ -339,13 +416,73 @@ def bench_infer1m(steps):
     lat = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]) * 1e3
     best = torch.gather(idx, -1, score.argmax(-1, keepdim=True))[..., 0, 0].cpu()
     hits = float((best == needles.view(steps, 1, 1, 1)).float().mean())
+    graph = bench_infer1m_graph(shape, lqs, qs, lkd, kd, vd, qpos, ws, idx, o, min(steps, 200))
     del kd, vd
     torch.cuda.empty_cache()
     return {"workload": name, "tokens": Nk * S, "steps": steps,
             "step_latency_us_p50": round(float(np.percentile(lat, 50)), 2),
             "step_latency_us_p99": round(float(np.percentile(lat, 99)), 2),
             "step_latency_us_mean": round(float(lat.mean()), 2),
-            "needle_hit_rate": hits}
+            "needle_hit_rate": hits, "hip_graph": graph}
+
+
+def bench_infer1m_graph(shape, lqs, qs, lkd, kd, vd, qpos, ws, idx_eager, o_eager, steps):
+    """The same retrieve + forward step captured once in a HIP graph (torch.cuda.CUDAGraph)
+    on static query buffers; each step's query chunk is copied into them before its replay
+    and only the replay is timed, steps back to back as in the eager loop.  The first 20
+    replays' idx and O must equal the eager steps' bits (checked on the host)."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    k, S = shape.top_k, shape.chunk_size
+    lq_s, q_s = torch.empty_like(lqs[0]), torch.empty_like(qs[0])
+    idx_s = torch.empty_like(idx_eager[0])
+    score_s = torch.empty(idx_s.shape, dtype=torch.float32, device="cuda")
+    w_s = torch.empty_like(score_s)
+    o_s = torch.empty_like(qs[0])
+    lse_s = torch.empty(tuple(idx_s.shape) + (S,), dtype=torch.float32, device="cuda")
+
+    def body():
+        gca.gca_retrieve(shape, lq_s, lkd, qpos, idx_s, score_s, w_s, ws=ws)
+        gca.gca_forward(shape, q_s, kd, vd, idx_s, w_s, o_s, lse_s)
+
+    lq_s.copy_(lqs[0])
+    q_s.copy_(qs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    exact = True
+    for s in range(20):  # replays checked against the eager steps, synchronised
+        lq_s.copy_(lqs[s])
+        q_s.copy_(qs[s])
+        g.replay()
+        torch.cuda.synchronize()
+        exact = exact and torch.equal(idx_s, idx_eager[s]) and torch.equal(o_s, o_eager[s])
+    # timed back to back like the eager steps: events around each replay only
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for s in range(steps):
+        lq_s.copy_(lqs[s])
+        q_s.copy_(qs[s])
+        ea[s].record()
+        g.replay()
+        eb[s].record()
+    torch.cuda.synchronize()
+    lat = [ea[s].elapsed_time(eb[s]) * 1e3 for s in range(steps)]
+    lat = np.array(lat)
+    del g
+    return {"steps": steps, "step_latency_us_p50": round(float(np.percentile(lat, 50)), 2),
+            "step_latency_us_p99": round(float(np.percentile(lat, 99)), 2),
+            "replays_equal_eager_bits": bool(exact)}
 
 
 def bench_infer1m_offload(steps):
@@ -534,6 +671,14 @@ def main():
         swa_res = bench_swa(args.steps)
         print(f"[bench] sliding-window attention step: {swa_res['ms_per_step']} ms",
               file=sys.stderr, flush=True)
+    extra = fwd16k = None
+    if not args.no_extras:
+        extra = bench_cold_and_copy(step)
+        print(f"[bench] cold step: {extra['cold_ms_per_step_median']} ms", file=sys.stderr,
+              flush=True)
+        fwd16k = bench_train16k_fwd(args.steps)
+        print(f"[bench] 16K forward (one group): {fwd16k['ms_per_step']} ms", file=sys.stderr,
+              flush=True)
     gumbel = None
     if not args.no_gumbel:
         bufs = (idx, score, w, o, lse, dq, dk, dv, dw, dscore, dlq, dlk, wsr, wsb)
@@ -577,6 +722,8 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "long_context": long_ctx or None,
+        "cold_and_copy": extra,
+        "train16k_fwd": fwd16k,
         "gumbel_train_step": gumbel,
         "sliding_window_step": swa_res,
         "wall_s_timed": round(wall, 3),

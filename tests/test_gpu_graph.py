@@ -1,0 +1,74 @@
+"""HIP-graph capture of the GCA step (torch.cuda.CUDAGraph on torch's stream):
+the library's calls enqueue only kernels, so one training step (retrieve +
+forward + backward) can be captured and replayed.  Every replay, with eager
+work and synchronisations between replays, must reproduce the eager step's
+outputs bit for bit (same kernels, same fixed summation order)."""
+
+import pytest
+import torch
+
+import retrieval_sparse_attention_amd as gca
+import synth
+from gpu_common import accept_for, dev, require_gpu, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_training_step_replays_match_eager():
+    name, over = "train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72)
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    G, B, H, Nq, k = shape.G, shape.B, shape.H, shape.n_query, shape.top_k
+    out = dict(idx=torch.empty((G, B, H, Nq, k), dtype=torch.int32, device="cuda"),
+               score=torch.empty((G, B, H, Nq, k), device="cuda"),
+               w=torch.empty((G, B, H, Nq, k), device="cuda"),
+               o=torch.empty_like(d["q"]),
+               lse=torch.empty((G, B, H, Nq, k, 64), device="cuda"),
+               dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]),
+               dv=torch.empty_like(d["v"]),
+               dw=torch.empty((G, B, H, Nq, k), device="cuda"),
+               dscore=torch.empty((G, B, H, Nq, k), device="cuda"),
+               dlq=torch.empty(tuple(d["lq"].shape), device="cuda"),
+               dlk=torch.empty(tuple(d["lk"].shape), device="cuda"))
+    wsr = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)),
+                      dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(gca.gca_workspace_size(shape, gca.OP_BACKWARD), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], out["idx"], out["score"],
+                         out["w"], ws=wsr)
+        gca.gca_forward(shape, d["q"], d["k"], d["v"], out["idx"], out["w"], out["o"],
+                        out["lse"])
+        gca.gca_backward(shape, d["q"], d["k"], d["v"], out["idx"], out["w"], out["lse"],
+                         d["dout"], d["lq"], d["lk"], out["dq"], out["dk"], out["dv"],
+                         out["dw"], out["dscore"], out["dlq"], out["dlk"], ws=wsb)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {key: val.clone() for key, val in out.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for val in out.values():
+            val.fill_(7)  # eager work between replays; every output must be rewritten
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, val in out.items():
+            assert torch.equal(val, eager[key]), (r, key)
