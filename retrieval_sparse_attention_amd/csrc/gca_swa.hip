@@ -244,16 +244,22 @@ __device__ __forceinline__ void swa_bwdq_tile(const SwaBwdQCtx& cx, int u, const
     for (int dt = 0; dt < 4; ++dt)
       ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
   const int j = cx.j_lo + u;
-  const bool edge = edge_tile(j, cx.t, cx.window);
-  const int base = 64 * (j - cx.t) - cx.x + 4 * grp;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float p = fast_exp2(fmaf(sacc[mt][r], cx.c2, -cx.l2));
-      if (edge && !in_window(base + 16 * mt + r, cx.window)) p = 0.0f;
-      sacc[mt][r] = p * (pacc[mt][r] - cx.dsum);  // dS
-    }
+    for (int r = 0; r < 4; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], cx.c2, -cx.l2));
+  if (edge_tile(j, cx.t, cx.window)) {  // wave-uniform: only 2 of the block's tiles
+    const int base = 64 * (j - cx.t) - cx.x + 4 * grp;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!in_window(base + 16 * mt + r, cx.window)) sacc[mt][r] = 0.0f;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sacc[mt][r] = sacc[mt][r] * (pacc[mt][r] - cx.dsum);  // dS
   // dQ^T (d x x) += K^T (d x j) dS^T (j x x)
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -399,14 +405,16 @@ __device__ __forceinline__ void swa_bwdkv_block(const SwaBwdKVCtx& cx, int u, fl
       const int x0 = 32 * kb + 16 * h + 4 * grp;
       const f32x4 l4 = *(const f32x4*)(l2r + x0);
       const f32x4 d4 = *(const f32x4*)(dr + x0);
-      const int base = 64 * (cx.j - t) + cx.jl - x0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float p = fast_exp2(fmaf(sacc[h][e], cx.c2, -l4[e]));
-        if (edge && !in_window(base - e, cx.window)) p = 0.0f;
-        sacc[h][e] = p;
-        pacc[h][e] = p * (pacc[h][e] - d4[e]);
+      for (int e = 0; e < 4; ++e) sacc[h][e] = fast_exp2(fmaf(sacc[h][e], cx.c2, -l4[e]));
+      if (edge) {  // wave-uniform: only 2 of the key block's query blocks
+        const int base = 64 * (cx.j - t) + cx.jl - x0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!in_window(base - e, cx.window)) sacc[h][e] = 0.0f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[h][e] = sacc[h][e] * (pacc[h][e] - d4[e]);
     }
     // dV^T (d x j) += dO^T (d x x) P (x x j);  dK^T (d x j) += Q^T (d x x) dS (x x j)
     bf16x8 bp, bs;
