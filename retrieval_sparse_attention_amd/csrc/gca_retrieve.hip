@@ -430,6 +430,9 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   // sets; it is cleared during round R + 2, after every wave has read it (two
   // barriers later) and before round R + 3 can set it again.  Rounds past the
   // slice (up to PF - 1 at the end) select nothing.
+  // this lane's query threshold, kept in a register: tau_raw changes only in
+  // round 0 and in a compaction, and both refresh it
+  float tl = -__builtin_huge_valf();
   for (int round0 = 0; round0 < n_rounds; round0 += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
@@ -455,7 +458,6 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
       const int64_t rem64 = lim - blk - 4 * half;
       const int rem = rem64 < 0 ? 0 : (rem64 > 32 ? 32 : (int)rem64);
       const bool whole = __all(rem >= 28);  // every row of the block is eligible
-      float tl = tau_raw[col];
       if (round == 0) {
         float m1 = -__builtin_huge_valf(), m2 = -__builtin_huge_valf();
 #pragma unroll
@@ -475,16 +477,27 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         tl = fmaxf(tl, NOISE ? b_raw : raw_bound(b_raw * score_scale + 0.0f, inv_scale));
         if (tid < 32) tau_raw[tid] = tl;  // lane tid < 32 holds query col = tid
       }
-      int nh = 0;
+      // Fast test: once tau has risen, most blocks hold no candidate at or
+      // above it; the lane's best eligible value decides with one compare.
+      float best = -__builtin_huge_valf();
       if (whole) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) nh += acc[r] >= tl ? 1 : 0;
+        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          nh += (acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem) ? 1 : 0;
+          best = fmaxf(best, (8 * (r >> 2) + (r & 3)) < rem ? acc[r] : -__builtin_huge_valf());
       }
-      if (__any(nh != 0)) {
+      if (__any(best >= tl)) {
+        int nh = 0;
+        if (whole) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) nh += acc[r] >= tl ? 1 : 0;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            nh += (acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem) ? 1 : 0;
+        }
         // One LDS atomic per lane reserves its entries; the writes then go out
         // without waiting on each other: a lane without a hit at r writes to
         // its spare slot past kScanCap, so branches stay uniform.
@@ -520,9 +533,11 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         if (nh && o > kScanCap - 128) full[round % 3] = 1;
       }
       __syncthreads();
-      if (round + 1 < n_rounds && full[round % 3])
+      if (round + 1 < n_rounds && full[round % 3]) {
         scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
                                   inv_scale);
+        tl = tau_raw[col];  // raised by the compaction
+      }
     }
   }
   scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale, inv_scale);
