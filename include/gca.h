@@ -14,6 +14,15 @@
  *   gca_forward   -- per-chunk attention of every token + weighted fusion
  *   gca_backward  -- gradients of Q, K, V, the weights, the scores and the
  *                    landmarks
+ * and the calls around them:
+ *   gca_retrieve_gumbel -- gca_retrieve with Gumbel-noised selection (training)
+ *   gca_gather_kv       -- packs the retrieved K/V tiles, e.g. out of pinned
+ *                          host memory, for K/V offloaded from the GPU
+ *   gca_swa_forward / gca_swa_backward -- the layer's causal sliding-window
+ *                          self-attention
+ * An upper layer group reuses one gca_retrieve (and one K/V) for all of its
+ * layers: each layer calls gca_forward / gca_backward with the same idx, w, K
+ * and V, and the shared tensors' gradients are the sums over the layers.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -202,8 +211,8 @@ gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void*
  *   q, k, v, o, dout, dq, dk, dv   [B, H, T, head_dim]   bf16, big
  *   lse                            [B, H, T]             float32
  * Supported: dtype GCA_BF16, head_dim 64, T a multiple of 64 (whole 64-token
- * chunks), window >= 1 (any value; windows >= T give causal attention),
- * B*H*T/64 < 2^31.  Same conventions, checks and errors as the GCA calls.
+ * chunks) below 2^30, window >= 1 (any value; windows >= T give causal
+ * attention), B*H*T/64 < 2^31.  Same conventions, checks and errors as the GCA calls.
  * gca_swa_backward needs a workspace of gca_swa_workspace_size bytes (D rows).
  */
 typedef struct {

@@ -355,6 +355,7 @@ static gca_status check_swa(const gca_swa_shape* s, int64_t* heads) {
   if (s->dtype != GCA_BF16 || s->head_dim != 64)
     return fail(GCA_ERR_UNSUPPORTED, "sliding-window attention needs bf16 and head_dim 64");
   if (s->T % 64 != 0) return fail(GCA_ERR_UNSUPPORTED, "T must be a multiple of 64");
+  if (s->T >= (int64_t(1) << 30)) return fail(GCA_ERR_UNSUPPORTED, "T must be below 2^30");
   int64_t h, rows;
   if (!mul_ok(s->B, s->H, &h) || !mul_ok(h, s->T, &rows) || rows > (int64_t(1) << 40))
     return fail(GCA_ERR_INVALID_ARGUMENT, "tensor sizes overflow");
@@ -388,7 +389,9 @@ gca_status gca_swa_forward(const gca_swa_shape* shape, const void* q, const void
   gca::LaunchSwa a{};
   a.heads = heads;
   a.n_tok = shape->T;
-  a.window = shape->window;
+  // a window past the sequence start is the same as one of T tokens; the
+  // kernels' block arithmetic then stays far inside 32-bit range
+  a.window = shape->window < shape->T ? shape->window : (int)shape->T;
   a.scale = shape->scale;
   a.q = q;
   a.kk = k;
@@ -426,7 +429,9 @@ gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const voi
   gca::LaunchSwa a{};
   a.heads = heads;
   a.n_tok = shape->T;
-  a.window = shape->window;
+  // a window past the sequence start is the same as one of T tokens; the
+  // kernels' block arithmetic then stays far inside 32-bit range
+  a.window = shape->window < shape->T ? shape->window : (int)shape->T;
   a.scale = shape->scale;
   a.q = q;
   a.kk = k;

@@ -158,3 +158,10 @@ def test_swa_checks_before_any_device_call():
     st, msg = _status("gca_swa_backward", ctypes.byref(ok), A, A, A, A, A, A, A, A, A, A,
                       ctypes.c_size_t(16), None)
     assert st == 3 and "workspace" in msg
+
+
+def test_swa_rejects_sequences_past_2_30():
+    n = ctypes.c_size_t(0)
+    big = gca.make_swa_shape(1, 1, 2 ** 30, 64, 512)
+    st, msg = _status("gca_swa_workspace_size", ctypes.byref(big), ctypes.byref(n))
+    assert st == 2 and "2^30" in msg

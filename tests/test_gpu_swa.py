@@ -47,6 +47,7 @@ def run_swa(shape, x, backward=True):
     (1, 2, 512, 64),     # window of exactly one block
     (1, 1, 384, 65),
     (1, 2, 256, 1),      # degenerate: every token sees itself only
+    (1, 1, 192, 2 ** 31 - 1),  # the largest window: clamped to T, causal attention
 ])
 def test_swa_parity(B, H, T, W):
     x = synth.swa_inputs(B, H, T, 64, seed=T + W)
