@@ -269,7 +269,7 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
   }
 }
 
-__global__ __launch_bounds__(256) void k_bwd_q_bf16(
+__global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
     const bf16* __restrict__ dout, const bf16* __restrict__ lk, bf16* __restrict__ dq,
