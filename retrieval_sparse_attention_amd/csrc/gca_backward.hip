@@ -440,14 +440,6 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
   if (u + 1 < nb) bwdkv_fetch(cx, u + 1, nx, qn, don);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    // dO^T and Q^T operands of this contraction step, requested first so
-    // that their LDS latency overlaps the products and arithmetic below.
-    bf16x8 ado[4], aq[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      ado[dt] = lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-      aq[dt] = lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-    }
     // S (x x j) = Q K_c^T and dP~ = dO V_c^T for query tiles 2kb, 2kb+1;
     // the lane holds rows x = 32kb + 16h + 4grp + r of its key column j.
     f32x4 sacc[2], pacc[2];
@@ -481,15 +473,23 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
       bs[e] = (bf16)pacc[0][e];
       bs[4 + e] = (bf16)pacc[1][e];
     }
+    // dO^T and Q^T operands, read right before their products: holding all
+    // eight across the arithmetic above would need 32 more registers, and at
+    // 128 registers four workgroups share a CU, whose other waves cover the
+    // LDS latency.
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      dvacc[dt] = mfma16x16x32(ado[dt], bp, dvacc[dt]);
-      dkacc[dt] = mfma16x16x32(aq[dt], bs, dkacc[dt]);
+      const bf16x8 ado =
+          lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      const bf16x8 aq =
+          lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      dvacc[dt] = mfma16x16x32(ado, bp, dvacc[dt]);
+      dkacc[dt] = mfma16x16x32(aq, bs, dkacc[dt]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void k_bwd_kv_bf16(
+__global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
