@@ -237,12 +237,6 @@ __device__ __forceinline__ void swa_bwdq_tile(const SwaBwdQCtx& cx, int u, const
       pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
     }
   }
-  bf16x8 ka[2][4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
   const int j = cx.j_lo + u;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -269,12 +263,17 @@ __device__ __forceinline__ void swa_bwdq_tile(const SwaBwdQCtx& cx, int u, const
       bs[e] = (bf16)sacc[2 * kb][e];
       bs[4 + e] = (bf16)sacc[2 * kb + 1][e];
     }
+    // K^T operands read right before their products (register budget of four
+    // workgroups per CU)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
+    for (int dt = 0; dt < 4; ++dt)
+      dqacc[dt] = mfma16x16x32(
+          lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane), bs,
+          dqacc[dt]);
   }
 }
 
-__global__ __launch_bounds__(256) void k_swa_bwd_q_bf16(
+__global__ __launch_bounds__(256, 4) void k_swa_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const float* __restrict__ lse, const bf16* __restrict__ dout,
     bf16* __restrict__ dq, float* __restrict__ delta, int64_t n_tok, int window, float scale) {
@@ -361,8 +360,12 @@ __device__ __forceinline__ void swa_bwdkv_fetch(const SwaBwdKVCtx& cx, int u, fl
   const int64_t t = cx.t_lo + u;
   cx.dma->copy_async(qd, cx.q_head + t * 4096);
   cx.dma->copy_async(dod, cx.do_head + t * 4096);
+  // both rows from wave-uniform bases (no per-lane 64-bit pointer kept live);
+  // threads 0..63 keep L, 64..127 keep D
   const int tid = cx.tid;
-  if (tid < 128) row = tid < 64 ? cx.lse_head[t * 64 + tid] : cx.d_head[t * 64 + (tid - 64)];
+  const float a = cx.lse_head[t * 64 + (tid & 63)];
+  const float b = cx.d_head[t * 64 + (tid & 63)];
+  row = tid < 64 ? a : b;
 }
 
 __device__ __forceinline__ void swa_bwdkv_block(const SwaBwdKVCtx& cx, int u, float& row,
@@ -384,12 +387,6 @@ __device__ __forceinline__ void swa_bwdkv_block(const SwaBwdKVCtx& cx, int u, fl
   const bool edge = edge_tile(cx.j, t, cx.window);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    bf16x8 ado[4], aq[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      ado[dt] = lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-      aq[dt] = lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
-    }
     // S (x x j) = Q K^T and dP = dO V^T for query rows x = 32kb + 16h + 4grp + r
     f32x4 sacc[2], pacc[2];
 #pragma unroll
@@ -425,15 +422,21 @@ __device__ __forceinline__ void swa_bwdkv_block(const SwaBwdKVCtx& cx, int u, fl
       bs[e] = (bf16)pacc[0][e];
       bs[4 + e] = (bf16)pacc[1][e];
     }
+    // dO^T and Q^T operands read right before their products (register
+    // budget of four workgroups per CU; the other waves cover the LDS latency)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      dvacc[dt] = mfma16x16x32(ado[dt], bp, dvacc[dt]);
-      dkacc[dt] = mfma16x16x32(aq[dt], bs, dkacc[dt]);
+      const bf16x8 ado =
+          lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      const bf16x8 aq =
+          lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      dvacc[dt] = mfma16x16x32(ado, bp, dvacc[dt]);
+      dkacc[dt] = mfma16x16x32(aq, bs, dkacc[dt]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void k_swa_bwd_kv_bf16(
+__global__ __launch_bounds__(256, 4) void k_swa_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, bf16* __restrict__ dk, bf16* __restrict__ dv,
