@@ -28,7 +28,9 @@
  * --------------------------------
  * - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *   never allocates or frees device memory.  Its only state is a thread-local
- *   error string and, while enabled, the event timing records below.
+ *   error string, while enabled the event timing records below, and, per
+ *   device, one stream and two events that gca_backward creates on first use
+ *   (default priority) and keeps until the process ends.
  * - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *   return without synchronising.
  * - All arrays are dense, contiguous, row-major, with the layouts given below.
@@ -292,6 +294,11 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
  *   dlk            [G, B, H, Nk, Dl]    float32 output or NULL
  *   ws / ws_bytes  workspace (gca_workspace_size op 2)
  * dlq needs lk; dlk needs lq.
+ *
+ * Streams: the call forks a second stream of the library (per device) off
+ * `stream` for the reverse index of the retrieved chunks, which runs beside
+ * the query-side kernel, and joins it back before the key-side kernel; to the
+ * caller the work is ordered on `stream` as usual (also under graph capture).
  */
 gca_status gca_backward(const gca_shape* shape, const void* q, const void* k,
                         const void* v, const int32_t* idx, const float* w,

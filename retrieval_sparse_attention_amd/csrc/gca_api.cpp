@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gca.h"
 #include "gca_launch.h"
@@ -200,6 +201,41 @@ gca_status readable_on_device(const void* p, const char* name, const void** dev)
     *dev = p;
   }
   return GCA_OK;
+}
+
+// Per-device side stream and fork/join events of gca_backward, created on
+// first use (default priority, non-blocking) and kept until the process ends.
+// The mutex covers the whole enqueue of a backward call, so that concurrent
+// callers never interleave records of the shared events.
+struct SideResources {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false, failed = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideResources g_side[kMaxDevices];
+
+// The calling thread's device's resources, or nullptr (then the backward
+// runs on the caller's stream alone).  Call with g_side_mu held.
+SideResources* side_resources() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  SideResources& r = g_side[dev];
+  if (!r.ready && !r.failed) {
+    if (hipStreamCreateWithFlags(&r.stream, hipStreamNonBlocking) == hipSuccess &&
+        hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&r.join, hipEventDisableTiming) == hipSuccess) {
+      r.ready = true;
+    } else {
+      (void)hipGetLastError();
+      r.failed = true;
+    }
+  }
+  return r.ready ? &r : nullptr;
 }
 
 #define GCA_TRY(expr)                 \
@@ -557,6 +593,12 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
   a.rev_off = (int32_t*)((char*)ws + wl.rev_off);
   a.rev_ent = (int32_t*)((char*)ws + wl.rev_ent);
   a.stream = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (SideResources* sr = side_resources()) {
+    a.side = sr->stream;
+    a.fork = sr->fork;
+    a.join = sr->join;
+  }
   return device_status(gca::launch_backward(a), a.stream, "gca_backward");
 }
 

@@ -747,13 +747,24 @@ __global__ __launch_bounds__(64) void k_bwd_kv_f32(
 hipError_t launch_backward(const LaunchBackward& a) {
   const int64_t heads = a.G * a.B * a.H;
   if (heads == 0) return hipSuccess;
+  // The reverse index is needed only by the key-side kernel: on the side
+  // stream it runs beside the query-side kernel (fork after everything the
+  // caller queued before, join before the key-side kernel).
+  const bool fork = a.side != nullptr;
+  const hipStream_t rs = fork ? a.side : a.stream;
+  hipError_t err;
+  if (fork) {
+    if ((err = hipEventRecord(a.fork, a.stream)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(a.side, a.fork, 0)) != hipSuccess) return err;
+  }
   {
-  KernelTimer timer(kKernReverseIndex, a.stream);
-  hipLaunchKernelGGL(k_reverse_index, dim3((unsigned)heads), dim3(512), 0, a.stream, a.idx,
+  KernelTimer timer(kKernReverseIndex, rs);
+  hipLaunchKernelGGL(k_reverse_index, dim3((unsigned)heads), dim3(512), 0, rs, a.idx,
                      a.n_query, a.n_key, a.k, a.rev_off, a.rev_ent);
   }
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (fork && (err = hipEventRecord(a.join, a.side)) != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
   if (a.dtype == 1) {
     if (qtiles > 0) {
@@ -765,6 +776,7 @@ hipError_t launch_backward(const LaunchBackward& a) {
                          a.attn_scale, a.score_scale);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
       hipLaunchKernelGGL(k_bwd_kv_bf16, dim3((unsigned)ktiles), dim3(256), 0, a.stream,
@@ -783,6 +795,7 @@ hipError_t launch_backward(const LaunchBackward& a) {
                          a.attn_scale, a.score_scale);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
       hipLaunchKernelGGL(k_bwd_kv_f32, dim3((unsigned)ktiles), dim3(64), 0, a.stream,
