@@ -180,9 +180,11 @@ gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void
  *   c in [0, n_key):  k_packed[g,b,h, t*k + i] = k[g,b,h,c] (one S x D tile),
  *                     v_packed likewise, idx_packed[g,b,h,t,i] = t*k + i
  *   otherwise:        zero tiles and idx_packed = -1.
- * gca_forward / gca_backward over (k_packed, v_packed, idx_packed) with a shape
- * whose n_key is n_query * top_k give the same results as over (k, v, idx):
+ * gca_forward over (k_packed, v_packed, idx_packed) with a shape whose n_key
+ * is n_query * top_k gives the same O and lse, bit for bit, as over (k, v, idx):
  * only k tiles per query chunk cross the host link instead of the whole K/V.
+ * (gca_backward over packed arrays returns dK/dV per packed row, i.e. per
+ * retrieved slot; summing the rows that hold chunk c gives dK/dV of chunk c.)
  *
  *   shape           G, B, H, n_query, n_key, chunk_size, head_dim, top_k, dtype
  *                   (the same limits as gca_forward)

@@ -145,3 +145,16 @@ def test_gather_full_size_infer1m_from_host():
         assert np.array_equal(ip.cpu().numpy(), ri)
         assert np.array_equal(_bits(kp), rk)
         assert np.array_equal(_bits(vp), rv)
+
+
+def test_gather_with_no_resident_chunks():
+    # n_key = 0: every slot is empty, k and v may be NULL
+    shape = gca.make_shape(1, 2, 2, 3, 0, 64, 64, 64, 4, gca.GCA_BF16, 0)
+    idx = torch.full((1, 2, 2, 3, 4), 5, dtype=torch.int32, device="cuda")
+    kp = torch.full((1, 2, 2, 12, 64, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, 7.0)
+    ip = torch.zeros((1, 2, 2, 3, 4), dtype=torch.int32, device="cuda")
+    gca.gca_gather_kv(shape, idx, None, None, kp, vp, ip)
+    torch.cuda.synchronize()
+    assert torch.all(ip == -1)
+    assert torch.all(kp == 0) and torch.all(vp == 0)
