@@ -57,12 +57,6 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  bf16x8 z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
-  return z;
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -255,25 +255,25 @@ __device__ __forceinline__ float tau_from_score(float t, float inv_scale) {
 //  2. Keys at or above that bound are packed to the front of the bucket.
 //  3. Each packed key's rank is the number of packed keys above it; ranks
 //     below k give the sorted top k.
-// Kept out of line: the scan loop that calls it then has no inner loops, and
-// the compiler keeps precise load-wait counts across its iterations.
+// Inlined into the plain scan (see scan_compact below).
 template <int KMAX, bool NOISE>
-__device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX],
-                                                       int* cnt, int* nkept, int* ncnt,
-                                                       float* tau_raw, int k, float score_scale,
-                                                       float inv_scale) {
+__device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*kept)[KMAX],
+                                                  int* cnt, int* nkept, int* ncnt, float* tau_raw,
+                                                  int k, float score_scale, float inv_scale) {
   constexpr int E = kScanCap / 8;
   constexpr int EK = (KMAX + 7) / 8;
   const int tid = threadIdx.x;
   const int q = tid >> 3, sub = tid & 7;
   ScanEntry* b = bucket + q * kScanStride;
   const int n = cnt[q], nk = nkept[q];
-  // entries per thread this wave needs (its 8 queries' largest bucket)
+  // entries per thread this wave needs (its 8 queries' largest bucket); the
+  // xor 8/16/32 maximum covers all 8 queries of the wave, so it is uniform and
+  // the loops below branch on a scalar
   int nw = n;
   nw = max(nw, __shfl_xor(nw, 8));
   nw = max(nw, __shfl_xor(nw, 16));
   nw = max(nw, __shfl_xor(nw, 32));
-  const int per = (nw + 7) >> 3;
+  const int per = __builtin_amdgcn_readfirstlane((nw + 7) >> 3);
   uint64_t e[E + EK];
 #pragma unroll
   for (int p = 0; p < E; ++p) {
@@ -302,14 +302,28 @@ __device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64
   thr = umin64(thr, shfl_xor64(thr, 4));
   if (sub == 0) ncnt[q] = 0;
   __syncthreads();
+  // Inlined, the pack has no branches: a key below thr (or empty) goes to the
+  // row's last slot, which no rank read reaches (n2 + 3 < kScanStride - 1).
   uint64_t* pk = (uint64_t*)b;  // packed keys reuse the bucket row
   int np = 0;
 #pragma unroll
   for (int p = 0; p < E + EK; ++p) np += (e[p] != 0 && e[p] >= thr) ? 1 : 0;
   int o = np ? atomicAdd(&ncnt[q], np) : 0;
+  wait_lds();
+  if constexpr (NOISE) {
+    // (out of line: the branchy form needs fewer registers)
 #pragma unroll
-  for (int p = 0; p < E + EK; ++p)
-    if (e[p] != 0 && e[p] >= thr) pk[o++] = e[p];
+    for (int p = 0; p < E + EK; ++p)
+      if (e[p] != 0 && e[p] >= thr) pk[o++] = e[p];
+  } else {
+#pragma unroll
+    for (int p = 0; p < E + EK; ++p) {
+      if (p < E && p >= per) continue;  // uniform: entries this wave never loaded
+      const bool keep = e[p] != 0 && e[p] >= thr;
+      pk[keep ? o : kScanStride - 1] = e[p];
+      o += keep ? 1 : 0;
+    }
+  }
   __syncthreads();
   const int n2 = ncnt[q];
   for (int u0 = 0; u0 < n2; u0 += 32) {
@@ -344,6 +358,33 @@ __device__ __attribute__((noinline)) void scan_compact(ScanEntry* bucket, uint64
                         : -__builtin_huge_valf();
   }
   __syncthreads();
+}
+
+template <int KMAX, bool NOISE>
+__device__ __attribute__((noinline)) void scan_compact_call(ScanEntry* bucket,
+                                                            uint64_t (*kept)[KMAX], int* cnt,
+                                                            int* nkept, int* ncnt, float* tau_raw,
+                                                            int k, float score_scale,
+                                                            float inv_scale) {
+  scan_compact_body<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
+                                 inv_scale);
+}
+
+// The plain scan inlines the compaction: as a call it waits for every landmark
+// load in flight on entry (the calling convention), saves registers to scratch
+// and reaches LDS through generic pointers, and inlined it takes about a
+// quarter less time.  The Gumbel scan keeps the call: its noise arithmetic
+// leaves no registers for the inlined body without spills.
+template <int KMAX, bool NOISE>
+__device__ __forceinline__ void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX], int* cnt,
+                                             int* nkept, int* ncnt, float* tau_raw, int k,
+                                             float score_scale, float inv_scale) {
+  if constexpr (NOISE)
+    scan_compact_call<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
+                                   inv_scale);
+  else
+    scan_compact_body<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
+                                   inv_scale);
 }
 
 template <int DL, int KMAX, bool NOISE>
@@ -398,12 +439,16 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   }
   if (tid < 3) full[tid] = 0;
 
+  // Query landmarks as the MFMA B operand.  Lanes past the last query read
+  // query 0's row and select nothing (their candidate count is 0).  The loads
+  // are unconditional: loads under a lane mask leave the compiler unsure how
+  // many loads are in flight, and it then drains every landmark block at the
+  // top of each round instead of keeping the next ones in flight.
   bf16x8 bq[NKS];
   {
     const bf16* row = lq + (head * n_query + (q_ok ? q : 0)) * DL + HALF * half;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      bq[ks] = q_ok ? *(const bf16x8*)(row + 8 * ks) : zero_bf16x8();
+    for (int ks = 0; ks < NKS; ++ks) bq[ks] = *(const bf16x8*)(row + 8 * ks);
   }
   const float inv_scale = 1.0f / score_scale;
 
@@ -431,8 +476,9 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   // barriers later) and before round R + 3 can set it again.  Rounds past the
   // slice (up to PF - 1 at the end) select nothing.
   // this lane's query threshold, kept in a register: tau_raw changes only in
-  // round 0 and in a compaction, and both refresh it
-  float tl = -__builtin_huge_valf();
+  // round 0 and in a compaction, and both refresh it.  It never drops below
+  // -FLT_MAX (a bound every finite score meets), so -inf marks ineligible rows.
+  float tl = -__FLT_MAX__;
   for (int round0 = 0; round0 < n_rounds; round0 += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
@@ -455,16 +501,22 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         }
       }
       // candidate blk + c_row(r, half) is eligible iff c_row(r, half) - 4*half < rem
-      const int64_t rem64 = lim - blk - 4 * half;
-      const int rem = rem64 < 0 ? 0 : (rem64 > 32 ? 32 : (int)rem64);
-      const bool whole = __all(rem >= 28);  // every row of the block is eligible
+      // (lim - blk fits in 32 bits: both lie in [0, n_key], n_key < 2^31).
+      // Ineligible rows become -inf, below every threshold (tl >= -FLT_MAX),
+      // so the tests below need no eligibility mask; only the blocks where a
+      // query's candidates end take this branch.
+      const int rem = min(max((int)(lim - blk) - 4 * half, 0), 32);
+      if (!__all(rem >= 28)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[r] = (8 * (r >> 2) + (r & 3)) < rem ? acc[r] : -__builtin_huge_valf();
+      }
       if (round == 0) {
         float m1 = -__builtin_huge_valf(), m2 = -__builtin_huge_valf();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float am = (8 * (r >> 2) + (r & 3)) < rem ? acc[r] : -__builtin_huge_valf();
-          if (KMAX > 8) m2 = fmaxf(m2, fminf(m1, am));
-          m1 = fmaxf(m1, am);
+          if (KMAX > 8) m2 = fmaxf(m2, fminf(m1, acc[r]));
+          m1 = fmaxf(m1, acc[r]);
         }
         atomicMin(&first_bound[col], ord_score(c_first == 2 ? m2 : m1));
         __syncthreads();
@@ -478,26 +530,14 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         if (tid < 32) tau_raw[tid] = tl;  // lane tid < 32 holds query col = tid
       }
       // Fast test: once tau has risen, most blocks hold no candidate at or
-      // above it; the lane's best eligible value decides with one compare.
-      float best = -__builtin_huge_valf();
-      if (whole) {
+      // above it; the lane's best value decides with one compare.
+      float best = acc[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) best = fmaxf(best, acc[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          best = fmaxf(best, (8 * (r >> 2) + (r & 3)) < rem ? acc[r] : -__builtin_huge_valf());
-      }
+      for (int r = 1; r < 16; ++r) best = fmaxf(best, acc[r]);
       if (__any(best >= tl)) {
         int nh = 0;
-        if (whole) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) nh += acc[r] >= tl ? 1 : 0;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            nh += (acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem) ? 1 : 0;
-        }
+        for (int r = 0; r < 16; ++r) nh += acc[r] >= tl ? 1 : 0;
         // One LDS atomic per lane reserves its entries; the writes then go out
         // without waiting on each other: a lane without a hit at r writes to
         // its spare slot past kScanCap, so branches stay uniform.
@@ -506,27 +546,14 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
         ScanEntry* bb = bucket + col * kScanStride;
         const int spare = kScanCap + half;
         const int j0 = (int)(blk + 4 * half);
-        if (whole) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool hit = acc[r] >= tl;
-            if (__any(hit)) {
-              ScanEntry* d = bb + (hit ? o : spare);
-              d->raw = acc[r];
-              d->j = j0 + 8 * (r >> 2) + (r & 3);
-              o += hit ? 1 : 0;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool hit = acc[r] >= tl && (8 * (r >> 2) + (r & 3)) < rem;
-            if (__any(hit)) {
-              ScanEntry* d = bb + (hit ? o : spare);
-              d->raw = acc[r];
-              d->j = j0 + 8 * (r >> 2) + (r & 3);
-              o += hit ? 1 : 0;
-            }
+        for (int r = 0; r < 16; ++r) {
+          const bool hit = acc[r] >= tl;
+          if (__any(hit)) {
+            ScanEntry* d = bb + (hit ? o : spare);
+            d->raw = acc[r];
+            d->j = j0 + 8 * (r >> 2) + (r & 3);
+            o += hit ? 1 : 0;
           }
         }
         // the last lane to append to a query sees its final count
@@ -536,7 +563,7 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
       if (round + 1 < n_rounds && full[round % 3]) {
         scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
                                   inv_scale);
-        tl = tau_raw[col];  // raised by the compaction
+        tl = fmaxf(tau_raw[col], -__FLT_MAX__);  // raised by the compaction
       }
     }
   }

@@ -147,6 +147,20 @@ def test_gumbel_bf16_sliced_scan_and_merge(k, dl):
     check_gumbel(lq, lk, q_pos.numpy(), k, shape.score_scale, 0, seed, got, True)
 
 
+def test_gumbel_bf16_long_slices():
+    # 96 heads of one query tile over 8192 candidates: eight slices of 1024
+    # (8 rounds each), so the bucket compacts inside a slice with noise on
+    B, H, n_query, n_key, k = 8, 12, 8, 8192, 8
+    g = torch.Generator().manual_seed(91)
+    lq = (torch.randn(1, B, H, n_query, 64, generator=g) * 0.125).to(torch.bfloat16)
+    lk = (torch.randn(1, B, H, n_key, 64, generator=g) * 0.125).to(torch.bfloat16)
+    q_pos = torch.tensor([n_key + 1] * 5 + [5000, 1500, 3], dtype=torch.int32)
+    shape = gca.make_shape(1, B, H, n_query, n_key, 64, 64, 64, k, gca.GCA_BF16, 1)
+    seed = 0xC0FFEE
+    got = run_gumbel(shape, seed, dev(lq), dev(lk), dev(q_pos))
+    check_gumbel(lq, lk, q_pos.numpy(), k, shape.score_scale, 1, seed, got, True)
+
+
 def test_gumbel_is_deterministic_and_plan_independent():
     n_query, dl, k = 24, 64, 8
     lq, lk = _sliced_inputs(n_query, 3000, dl, seed=3)

@@ -82,9 +82,16 @@ def test_bf16_landmark_dim_32():
     _full_path("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=40, n_key=40, Dl=32)
 
 
-def test_bf16_sliced_scan_with_needles():
+@pytest.mark.parametrize("over", [
+    dict(n_key=5000, n_query=37, H=2, q_pos=5001),
+    # 96 heads x 2 query tiles: four slices of 2304 candidates (18 rounds each)
+    dict(n_key=9000, n_query=40, B=8, H=12, q_pos=9001),
+    # one head: 512 slices of one round; the merge takes 4096 partial keys per query
+    dict(n_key=65536, n_query=20, H=1, q_pos=65537),
+    dict(n_key=65536, n_query=20, H=1, q_pos=65537, k=16),
+], ids=["short_slices", "long_slices", "many_slices", "many_slices_k16"])
+def test_bf16_sliced_scan_with_needles(over):
     """n_key > 1024 takes the sliced scan + merge path; planted needles rank 1."""
-    over = dict(n_key=5000, n_query=37, H=2, q_pos=5001)
     cfg = synth.workload("retrieve16m", **over)
     lk = synth.context_landmarks("retrieve16m", **over)
     qb = synth.query_batch("retrieve16m", lk, accept=accept_for(cfg), **over)
