@@ -402,6 +402,9 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   __shared__ int cnt[32], nkept[32], ncnt[32];
   __shared__ float tau_raw[32];  // raw dot-product bound of the k-th best score
   __shared__ uint32_t first_bound[32];  // min over groups of the ordered c-th best dot product
+  // running maximum of each of the 8 lanes (4 waves x 2 halves) that hold a
+  // query's candidates: [query][2 wave + half]
+  __shared__ __align__(16) float run_max[32][8];
   __shared__ int full[3];  // per round (mod 3): some bucket may overflow next round
 
   const int tid = threadIdx.x;
@@ -479,6 +482,13 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
   // round 0 and in a compaction, and both refresh it.  It never drops below
   // -FLT_MAX (a bound every finite score meets), so -inf marks ineligible rows.
   float tl = -__FLT_MAX__;
+  // Running bound (k <= 8): the 8 lanes of a query see disjoint candidates, so
+  // the smallest of their running maxima is reached by 8 distinct candidates
+  // and bounds the k-th best from below.  It rises every round, between the
+  // compactions that set tau exactly; the maxima of round R are read in round
+  // R + 1, after the barrier that ends round R.
+  constexpr bool run_bound = KMAX <= 8;  // k <= KMAX
+  float rmax = -__builtin_huge_valf();
   for (int round0 = 0; round0 < n_rounds; round0 += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
@@ -534,6 +544,17 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
       float best = acc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) best = fmaxf(best, acc[r]);
+      if (run_bound) {
+        if (round > 0) {
+          const f32x4 rm_lo = *(const f32x4*)&run_max[col][0];
+          const f32x4 rm_hi = *(const f32x4*)&run_max[col][4];
+          const float rb = fminf(fminf(fminf(rm_lo[0], rm_lo[1]), fminf(rm_lo[2], rm_lo[3])),
+                                 fminf(fminf(rm_hi[0], rm_hi[1]), fminf(rm_hi[2], rm_hi[3])));
+          tl = fmaxf(tl, NOISE ? rb : raw_bound(rb * score_scale + 0.0f, inv_scale));
+        }
+        rmax = fmaxf(rmax, best);
+        run_max[col][2 * wave + half] = rmax;
+      }
       if (__any(best >= tl)) {
         int nh = 0;
 #pragma unroll
@@ -563,7 +584,7 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
       if (round + 1 < n_rounds && full[round % 3]) {
         scan_compact<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
                                   inv_scale);
-        tl = fmaxf(tau_raw[col], -__FLT_MAX__);  // raised by the compaction
+        tl = fmaxf(tl, tau_raw[col]);  // raised by the compaction
       }
     }
   }
