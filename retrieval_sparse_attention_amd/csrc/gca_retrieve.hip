@@ -245,8 +245,14 @@ __device__ __forceinline__ float tau_from_score(float t, float inv_scale) {
   return NOISE ? t : raw_bound(t, inv_scale);
 }
 
+// Completes this wave's LDS accesses before any later one issues; the compiler
+// moves no memory access across it.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Exact top k of every query's kept list plus its bucket (256 threads: 8 per
-// query, all in one wave).  Afterwards kept[q] holds the sorted top-k keys,
+// query, all in one wave).  Everything of query q (bucket row, kept list,
+// counts, tau) is touched only by its 8 threads, so the steps order within
+// the wave; one workgroup barrier at the end publishes the result.  Afterwards kept[q] holds the sorted top-k keys,
 // the bucket is empty and tau_raw[q] bounds the k-th best from below.
 //  1. Thread `sub` of query q takes bucket entries sub, sub+8, ... and kept
 //     entries sub, sub+8, and finds its c-th best key (c = 1 for k <= 8, else
@@ -301,7 +307,7 @@ __device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*
   thr = umin64(thr, shfl_xor64(thr, 2));
   thr = umin64(thr, shfl_xor64(thr, 4));
   if (sub == 0) ncnt[q] = 0;
-  __syncthreads();
+  wave_lds_sync();
   // Inlined, the pack has no branches: a key below thr (or empty) goes to the
   // row's last slot, which no rank read reaches (n2 + 3 < kScanStride - 1).
   uint64_t* pk = (uint64_t*)b;  // packed keys reuse the bucket row
@@ -324,7 +330,7 @@ __device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*
       o += keep ? 1 : 0;
     }
   }
-  __syncthreads();
+  wave_lds_sync();
   const int n2 = ncnt[q];
   for (int u0 = 0; u0 < n2; u0 += 32) {
     uint64_t mine[4];
@@ -349,7 +355,7 @@ __device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*
     for (int u = 0; u < 4; ++u)
       if (mine[u] != 0 && rank[u] < k) kept[q][rank[u]] = mine[u];
   }
-  __syncthreads();
+  wave_lds_sync();
   const int m = n2 < k ? n2 : k;
   if (sub == 0) {
     cnt[q] = 0;
