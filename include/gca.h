@@ -288,14 +288,15 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
  *   idx, w         [G, B, H, Nq, k]     int32 / float32 (as passed to forward)
  *   lse            [G, B, H, Nq, k, S]  float32 from gca_forward
  *   lq, lk         landmarks as in gca_retrieve; may be NULL only if dlq/dlk
- *                  (respectively dlk/dlq) are NULL
+ *                  (respectively dlk/dlq) are NULL; lk is never read when
+ *                  n_key = 0 (every slot is then empty and dlq = 0)
  *   dq             [G, B, H, Nq, S, D]  dtype output
  *   dk, dv         [G, B, H, Nk, S, D]  dtype output
  *   dw, dscore     [G, B, H, Nq, k]     float32 output
  *   dlq            [G, B, H, Nq, Dl]    float32 output or NULL
  *   dlk            [G, B, H, Nk, Dl]    float32 output or NULL
  *   ws / ws_bytes  workspace (gca_workspace_size op 2)
- * dlq needs lk; dlk needs lq.
+ * dlq needs lk (unless n_key = 0); dlk needs lq.
  *
  * Streams: the call forks a second stream of the library (per device) off
  * `stream` for the reverse index of the retrieved chunks, which runs beside

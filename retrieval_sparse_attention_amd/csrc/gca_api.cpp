@@ -551,7 +551,9 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
   }
   GCA_TRY(opt(dlq, "dlq", 4));
   GCA_TRY(opt(dlk, "dlk", 4));
-  if (dlq != nullptr && z.q_rows > 0) GCA_TRY(need(lk, "lk (needed for dlq)", 16));
+  // dlq sums over retrieved chunks' landmarks: with no resident chunk it is 0
+  if (dlq != nullptr && z.q_rows > 0 && shape->n_key > 0)
+    GCA_TRY(need(lk, "lk (needed for dlq)", 16));
   if (dlk != nullptr && z.k_rows > 0) GCA_TRY(need(lq, "lq (needed for dlk)", 16));
   GCA_TRY(opt(lq, "lq", 16));
   GCA_TRY(opt(lk, "lk", 16));
@@ -581,7 +583,7 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
   a.lse = lse;
   a.dout = dout;
   a.lq = dlk ? lq : nullptr;
-  a.lk = dlq ? lk : nullptr;
+  a.lk = (dlq && shape->n_key > 0) ? lk : nullptr;  // no resident chunk: dlq = 0, lk unread
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
 }
 
 // Score / landmark epilogue of one query chunk, run by the whole workgroup.
-// dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq.
+// dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq.  With
+// no resident chunk (lk_head null) every slot is empty and dlq is 0.
 template <typename LT>
 __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_c,
                                const float* wv, float* dw_slot, float* ds_slot,
@@ -155,7 +156,9 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
     }
   }
   __syncthreads();
-  if (dlq_row) {
+  if (dlq_row && !lk_head) {
+    for (int d = tid; d < dl; d += nthreads) dlq_row[d] = 0.0f;
+  } else if (dlq_row) {
     for (int d = tid; d < dl; d += nthreads) {
       float acc = 0.0f;
 #pragma unroll

@@ -200,3 +200,28 @@ def test_bf16_scan_adversarial_orders(order, k, sliced):
     assert np.array_equal(idx.cpu().numpy(), r_idx)
     close("score", f64(score), r_score, True)
     close("w", f64(w), r_w, True)
+
+
+def test_bf16_no_resident_chunks():
+    """n_key = 0: every slot is empty; O = 0, lse = -inf and all gradients 0, with
+    NULL K/V/lk (zero-size tensors) and dlq still requested."""
+    cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=5, n_key=0)
+    shape = shape_of(cfg)
+    rng = np.random.default_rng(7)
+    lq = dev(torch.from_numpy(rng.standard_normal((1, 1, 2, 5, 64)).astype(np.float32) / 8)
+             .bfloat16())
+    q = dev(torch.from_numpy(rng.standard_normal((1, 1, 2, 5, 64, 64)).astype(np.float32) / 8)
+            .bfloat16())
+    dout = dev(torch.from_numpy(rng.standard_normal((1, 1, 2, 5, 64, 64)).astype(np.float32))
+               .bfloat16())
+    lk = torch.empty((1, 1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((1, 1, 2, 0, 64, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    q_pos = dev(torch.tensor([0, 1, 2, 3, 100], dtype=torch.int32))
+    idx, score, w = run_retrieve(shape, lq, lk, q_pos)
+    assert (idx.cpu() == -1).all() and (score.cpu() == 0).all() and (w.cpu() == 0).all()
+    o, lse = run_forward(shape, q, k, v, idx, w)
+    assert (o.float().cpu() == 0).all() and torch.isneginf(lse.cpu()).all()
+    g = run_backward(shape, q, k, v, idx, w, lse, dout, lq, lk)
+    for key in ("dq", "dw", "dscore", "dlq"):
+        assert (g[key].float().cpu() == 0).all(), key
