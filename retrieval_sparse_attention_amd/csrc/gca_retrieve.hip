@@ -211,8 +211,9 @@ __device__ __forceinline__ void keys_to_list(const uint64_t* keys, int m, float 
 // top k and raises tau to the k-th best.  In the first round, where no tau
 // exists yet, each of the 8 groups of 16 candidates a query gets (4 waves x 2
 // lane halves) offers its c-th best (c = 1 for k <= 8, else 2) and the
-// smallest offer serves as tau: 8c >= k candidates reach it.  Exactness never
-// depends on tau's quality, only the amount of work does.
+// smallest offer serves as tau: 8c >= k candidates reach it.  For k <= 8 the
+// same bound is refreshed every round from the 8 lanes' running maxima.
+// Exactness never depends on tau's quality, only the amount of work does.
 // ---------------------------------------------------------------------------
 constexpr int kScanCap = 160;  // bucket entries per query (>= 128 + 16)
 // Row stride in 8-byte entries: room past kScanCap for the packed kept keys
@@ -247,13 +248,16 @@ __device__ __forceinline__ float tau_from_score(float t, float inv_scale) {
 
 // Completes this wave's LDS accesses before any later one issues; the compiler
 // moves no memory access across it.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
 
 // Exact top k of every query's kept list plus its bucket (256 threads: 8 per
 // query, all in one wave).  Everything of query q (bucket row, kept list,
 // counts, tau) is touched only by its 8 threads, so the steps order within
-// the wave; one workgroup barrier at the end publishes the result.  Afterwards kept[q] holds the sorted top-k keys,
-// the bucket is empty and tau_raw[q] bounds the k-th best from below.
+// the wave; one workgroup barrier at the end publishes the result.
+// Afterwards kept[q] holds the sorted top-k keys, the bucket is empty and
+// tau_raw[q] bounds the k-th best from below.
 //  1. Thread `sub` of query q takes bucket entries sub, sub+8, ... and kept
 //     entries sub, sub+8, and finds its c-th best key (c = 1 for k <= 8, else
 //     2); the minimum over the 8 threads bounds the k-th best key from below
