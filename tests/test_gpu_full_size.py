@@ -89,6 +89,17 @@ def test_full_train16k_fwdbwd_two_groups():
     for (gg, b, h) in heads:
         for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
             close(f"{key}[{gg},{b},{h}]", f64(g[key][gg, b, h]), r[key][gg, b, h], True)
+    # the whole step again: every output, all 96 heads, bit for bit (the backward
+    # sums in a fixed order, with no floating-point atomics)
+    idx2, score2, w2 = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
+    o2, lse2 = run_forward(shape, d["q"], d["k"], d["v"], idx2, w2)
+    g2 = run_backward(shape, d["q"], d["k"], d["v"], idx2, w2, lse2, d["dout"], d["lq"], d["lk"])
+    torch.cuda.synchronize()
+    for name_, a_, b_ in (("idx", idx, idx2), ("score", score, score2), ("w", w, w2), ("o", o, o2),
+                          ("lse", lse, lse2)):
+        assert torch.equal(a_, b_), f"{name_} differs between two identical steps"
+    for key in g:
+        assert torch.equal(g[key], g2[key]), f"{key} differs between two identical steps"
 
 
 def test_full_infer1m_steps():
