@@ -220,10 +220,13 @@ constexpr int kScanCap = 160;  // bucket entries per query (>= 128 + 16)
 // and 2 spare slots, and odd, so the 32 rows a wave appends to at the same
 // position fall in 32 different bank pairs.
 constexpr int kScanStride = kScanCap + 25;
+// Landmark blocks in flight per wave.  One suffices: the next block's load
+// overlaps the current round's selection, and a second one costs registers
+// and loop unrolling (16M scan: 84 us with one, 90 us with two).
 #ifndef GCA_SCAN_PREFETCH
-#define GCA_SCAN_PREFETCH 2
+#define GCA_SCAN_PREFETCH 1
 #endif
-constexpr int kScanPrefetch = GCA_SCAN_PREFETCH;  // landmark blocks in flight per wave
+constexpr int kScanPrefetch = GCA_SCAN_PREFETCH;
 
 // Bucket entries hold the raw dot product (with noise: the perturbed score
 // itself) and the chunk index of a candidate; the selection key is formed only
@@ -265,11 +268,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 //  2. Keys at or above that bound are packed to the front of the bucket.
 //  3. Each packed key's rank is the number of packed keys above it; ranks
 //     below k give the sorted top k.
-// Inlined into the plain scan (see scan_compact below).
+// Inlined: as a call it waits for every landmark load in flight on entry (the
+// calling convention), saves registers to scratch and reaches LDS through
+// generic pointers; inlined it takes about a quarter less time.
 template <int KMAX, bool NOISE>
-__device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*kept)[KMAX],
-                                                  int* cnt, int* nkept, int* ncnt, float* tau_raw,
-                                                  int k, float score_scale, float inv_scale) {
+__device__ __forceinline__ void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX], int* cnt,
+                                             int* nkept, int* ncnt, float* tau_raw, int k,
+                                             float score_scale, float inv_scale) {
   constexpr int E = kScanCap / 8;
   constexpr int EK = (KMAX + 7) / 8;
   const int tid = threadIdx.x;
@@ -312,27 +317,20 @@ __device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*
   thr = umin64(thr, shfl_xor64(thr, 4));
   if (sub == 0) ncnt[q] = 0;
   wave_lds_sync();
-  // Inlined, the pack has no branches: a key below thr (or empty) goes to the
-  // row's last slot, which no rank read reaches (n2 + 3 < kScanStride - 1).
+  // The pack has no branches: a key below thr (or empty) goes to the row's
+  // last slot, which no rank read reaches (n2 + 3 < kScanStride - 1).
   uint64_t* pk = (uint64_t*)b;  // packed keys reuse the bucket row
   int np = 0;
 #pragma unroll
   for (int p = 0; p < E + EK; ++p) np += (e[p] != 0 && e[p] >= thr) ? 1 : 0;
   int o = np ? atomicAdd(&ncnt[q], np) : 0;
   wait_lds();
-  if constexpr (NOISE) {
-    // (out of line: the branchy form needs fewer registers)
 #pragma unroll
-    for (int p = 0; p < E + EK; ++p)
-      if (e[p] != 0 && e[p] >= thr) pk[o++] = e[p];
-  } else {
-#pragma unroll
-    for (int p = 0; p < E + EK; ++p) {
-      if (p < E && p >= per) continue;  // uniform: entries this wave never loaded
-      const bool keep = e[p] != 0 && e[p] >= thr;
-      pk[keep ? o : kScanStride - 1] = e[p];
-      o += keep ? 1 : 0;
-    }
+  for (int p = 0; p < E + EK; ++p) {
+    if (p < E && p >= per) continue;  // uniform: entries this wave never loaded
+    const bool keep = e[p] != 0 && e[p] >= thr;
+    pk[keep ? o : kScanStride - 1] = e[p];
+    o += keep ? 1 : 0;
   }
   wave_lds_sync();
   const int n2 = ncnt[q];
@@ -368,33 +366,6 @@ __device__ __forceinline__ void scan_compact_body(ScanEntry* bucket, uint64_t (*
                         : -__builtin_huge_valf();
   }
   __syncthreads();
-}
-
-template <int KMAX, bool NOISE>
-__device__ __attribute__((noinline)) void scan_compact_call(ScanEntry* bucket,
-                                                            uint64_t (*kept)[KMAX], int* cnt,
-                                                            int* nkept, int* ncnt, float* tau_raw,
-                                                            int k, float score_scale,
-                                                            float inv_scale) {
-  scan_compact_body<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
-                                 inv_scale);
-}
-
-// The plain scan inlines the compaction: as a call it waits for every landmark
-// load in flight on entry (the calling convention), saves registers to scratch
-// and reaches LDS through generic pointers, and inlined it takes about a
-// quarter less time.  The Gumbel scan keeps the call: its noise arithmetic
-// leaves no registers for the inlined body without spills.
-template <int KMAX, bool NOISE>
-__device__ __forceinline__ void scan_compact(ScanEntry* bucket, uint64_t (*kept)[KMAX], int* cnt,
-                                             int* nkept, int* ncnt, float* tau_raw, int k,
-                                             float score_scale, float inv_scale) {
-  if constexpr (NOISE)
-    scan_compact_call<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
-                                   inv_scale);
-  else
-    scan_compact_body<KMAX, NOISE>(bucket, kept, cnt, nkept, ncnt, tau_raw, k, score_scale,
-                                   inv_scale);
 }
 
 template <int DL, int KMAX, bool NOISE>
