@@ -615,11 +615,13 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
 // Merge of the per-slice lists: one wave per (head, query) row, n = nsplit *
 // KMAX keys (0 = empty).  The k-th largest of the 64 lane maxima bounds the
 // k-th best key from below; entries at or above it are packed into LDS and
-// ranked exactly.
+// ranked exactly.  With MW > 0 (n <= 64 MW) every key of the row is loaded
+// into registers at once, so the row costs one round trip to memory; with
+// MW = 0 the keys are streamed twice, 256 at a time.
 // ---------------------------------------------------------------------------
 constexpr int kMergeMax = 4096;  // nsplit * KMAX limit (LDS list size)
 
-template <int KMAX, bool NOISE>
+template <int KMAX, bool NOISE, int MW>
 __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ part, int n,
                                                    int k, int softmax_one,
                                                    int32_t* __restrict__ idx_out,
@@ -636,16 +638,30 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
   const uint64_t* src = part + qrow * n;
 
   uint64_t mx = 0;
-  for (int e0 = 0; e0 < n; e0 += 256) {
-    uint64_t v[4];
+  uint64_t reg[MW > 0 ? MW : 1];  // MW > 0: key lane + 64 u of the row
+  if (MW > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + lane + 64 * u;
-      v[u] = src[e < n ? e : n - 1];
-      v[u] = e < n ? v[u] : 0;
+    for (int u = 0; u < MW; ++u) {
+      const int e = lane + 64 * u;
+      reg[u] = src[e < n ? e : n - 1];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) mx = umax64(mx, v[u]);
+    for (int u = 0; u < MW; ++u) {
+      reg[u] = lane + 64 * u < n ? reg[u] : 0;
+      mx = umax64(mx, reg[u]);
+    }
+  } else {
+    for (int e0 = 0; e0 < n; e0 += 256) {
+      uint64_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + lane + 64 * u;
+        v[u] = src[e < n ? e : n - 1];
+        v[u] = e < n ? v[u] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = umax64(mx, v[u]);
+    }
   }
   // rank of this lane's maximum among the 64 (ties between empty lanes broken
   // by lane number), then the maximum of rank k-1
@@ -664,22 +680,28 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
   const uint64_t thr = ((uint64_t)thr_hi << 32) | thr_lo;
 
   int n2 = 0;
-  for (int e0 = 0; e0 < n; e0 += 256) {
-    uint64_t v[4];
+  auto pack = [&](uint64_t key) {
+    const bool pass = key != 0 && key >= thr;
+    const uint64_t mask = __ballot(pass);
+    const int pos = n2 + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+    if (pass) lst[pos] = key;
+    n2 += __builtin_popcountll(mask);
+  };
+  if (MW > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + lane + 64 * u;
-      v[u] = src[e < n ? e : n - 1];
-      v[u] = e < n ? v[u] : 0;
-    }
+    for (int u = 0; u < MW; ++u) pack(reg[u]);
+  } else {
+    for (int e0 = 0; e0 < n; e0 += 256) {
+      uint64_t v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool pass = v[u] != 0 && v[u] >= thr;
-      const uint64_t mask = __ballot(pass);
-      const int pos = n2 + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-      if (pass) lst[pos] = v[u];
-      n2 += __builtin_popcountll(mask);
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + lane + 64 * u;
+        v[u] = src[e < n ? e : n - 1];
+        v[u] = e < n ? v[u] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pack(v[u]);
     }
   }
   __syncthreads();
@@ -783,10 +805,18 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t rows = heads * a.n_query;
     KernelTimer timer(kKernMerge, a.stream);
-    hipLaunchKernelGGL((k_topk_merge<KMAX, NOISE>), dim3((unsigned)rows), dim3(64), 0, a.stream,
-                       a.part, pl.nsplit * KMAX, a.k, a.softmax_one, a.idx, a.score, a.w,
-                       (const bf16*)a.lq, (const bf16*)a.lk, a.n_query, a.n_key, a.dl,
-                       a.score_scale);
+    const int n = pl.nsplit * KMAX;
+    auto merge = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(64), 0, a.stream, a.part, n, a.k,
+                         a.softmax_one, a.idx, a.score, a.w, (const bf16*)a.lq,
+                         (const bf16*)a.lk, a.n_query, a.n_key, a.dl, a.score_scale);
+    };
+    if (n <= 512)
+      merge(k_topk_merge<KMAX, NOISE, 8>);
+    else if (n <= 1024)
+      merge(k_topk_merge<KMAX, NOISE, 16>);
+    else
+      merge(k_topk_merge<KMAX, NOISE, 0>);
     return hipGetLastError();
   }
   const int64_t rows = heads * a.n_query;

@@ -89,7 +89,13 @@ def test_bf16_landmark_dim_32():
     # one head: 512 slices of one round; the merge takes 4096 partial keys per query
     dict(n_key=65536, n_query=20, H=1, q_pos=65537),
     dict(n_key=65536, n_query=20, H=1, q_pos=65537, k=16),
-], ids=["short_slices", "long_slices", "many_slices", "many_slices_k16"])
+    # merge widths: 101 slices x 8 = 808 keys (registers, ragged last slice),
+    # 64 x 16 = 1024 (registers, full), 200 x 8 = 1600 (streamed, ragged)
+    dict(n_key=12900, n_query=20, H=1, q_pos=12901),
+    dict(n_key=8192, n_query=20, H=1, q_pos=8193, k=16),
+    dict(n_key=25500, n_query=20, H=1, q_pos=25501),
+], ids=["short_slices", "long_slices", "many_slices", "many_slices_k16", "merge_808",
+        "merge_1024_k16", "merge_1600"])
 def test_bf16_sliced_scan_with_needles(over):
     """n_key > 1024 takes the sliced scan + merge path; planted needles rank 1."""
     cfg = synth.workload("retrieve16m", **over)
