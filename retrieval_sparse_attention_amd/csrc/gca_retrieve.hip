@@ -215,6 +215,15 @@ __device__ __forceinline__ void keys_to_list(const uint64_t* keys, int m, float 
 // same bound is refreshed every round from the 8 lanes' running maxima.
 // Exactness never depends on tau's quality, only the amount of work does.
 // ---------------------------------------------------------------------------
+// Rows of the 32-row block at blk that lie below lim, for the lane half whose
+// rows start 4*half in, clamped to [0, 32].  Formed in 64 bits: blk passes
+// n_key by up to a round in the last blocks, so lim - blk can fall below
+// -2^31 when n_key is close to 2^31.
+__device__ __forceinline__ int eligible_rows(int64_t lim, int64_t blk, int half) {
+  const int64_t r = lim - blk - 4 * half;
+  return r <= 0 ? 0 : (r >= 32 ? 32 : (int)r);
+}
+
 constexpr int kScanCap = 160;  // bucket entries per query (>= 128 + 16)
 // Row stride in 8-byte entries: room past kScanCap for the packed kept keys
 // and 2 spare slots, and odd, so the 32 rows a wave appends to at the same
@@ -491,12 +500,11 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
             acc[4 * g4 + e] = fmaf(acc[4 * g4 + e], score_scale, gumbel_from_word(nz.w[e]));
         }
       }
-      // candidate blk + c_row(r, half) is eligible iff c_row(r, half) - 4*half < rem
-      // (lim - blk fits in 32 bits: both lie in [0, n_key], n_key < 2^31).
+      // candidate blk + c_row(r, half) is eligible iff c_row(r, half) - 4*half < rem.
       // Ineligible rows become -inf, below every threshold (tl >= -FLT_MAX),
       // so the tests below need no eligibility mask; only the blocks where a
       // query's candidates end take this branch.
-      const int rem = min(max((int)(lim - blk) - 4 * half, 0), 32);
+      const int rem = eligible_rows(lim, blk, half);
       if (!__all(rem >= 28)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)

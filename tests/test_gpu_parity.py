@@ -112,6 +112,38 @@ def test_bf16_sliced_scan_with_needles(over):
     assert (best == qb["needle"].numpy()[None, None, None, :]).all()
 
 
+@pytest.mark.parametrize("k,dl", [(8, 64), (16, 64), (4, 32)], ids=["k8", "k16", "k4_dl32"])
+def test_bf16_long_slices_mixed_positions(k, dl):
+    """Sliced scan + merge where the queries of a tile end at different
+    positions: none, one, fewer than k, inside the first slice, at and past
+    slice edges, all.  48 heads x 2 query tiles: 8 slices of 2560 candidates."""
+    from oracle import condition
+    B, H, nq, nk = 4, 12, 50, 20000
+    cfg = synth.workload("retrieve16m", B=B, H=H, n_query=nq, n_key=nk, k=k, Dl=dl)
+    rng = np.random.default_rng(40 + k + dl)
+    lq = torch.from_numpy((rng.standard_normal((1, B, H, nq, dl)) / 8).astype(np.float32))
+    lk = torch.from_numpy((rng.standard_normal((1, B, H, nk, dl)) / 8).astype(np.float32))
+    lq, lk = lq.bfloat16(), lk.bfloat16()
+    q_pos = rng.integers(0, nk + 2, size=nq).astype(np.int32)
+    q_pos[:8] = [0, 1, 2 + k // 2, 1000, 1300, 5121, nk, nk + 1]
+    q_pos[40:44] = [3, 700, 2600, 19000]
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(lq), dev(lk), dev(torch.from_numpy(q_pos)))
+    lq64, lk64 = f64(lq), f64(lk)
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, q_pos, k, cfg["score_scale"],
+                                       cfg["softmax_one"])
+    # rows whose k-th and (k+1)-th scores lie within float32 rounding of each
+    # other may order either way; 1e-5 is far above that (|score| < 2 here)
+    n_cand = np.clip(q_pos.astype(np.int64) - 1, 0, nk)
+    sep = np.stack([condition.gap_ok(lq64[0, b, h], lk64[0, b, h], n_cand, k,
+                                     cfg["score_scale"], 1e-5)
+                    for b in range(B) for h in range(H)]).reshape(1, B, H, nq)
+    assert sep.mean() > 0.95
+    assert np.array_equal(idx.cpu().numpy()[sep], r_idx[sep])
+    close("score", f64(score), r_score, True, mask=sep)
+    close("w", f64(w), r_w, True, mask=sep)
+
+
 def test_bf16_edge_positions():
     """q_pos giving 0, fewer than k, exactly k and all candidates; n_key not a multiple of 32."""
     cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=6, n_key=45)
