@@ -136,6 +136,10 @@ gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes);
  *   score [G, B, H, Nq, k]    float32 output
  *   w     [G, B, H, Nq, k]    float32 output
  *   ws / ws_bytes             workspace (gca_workspace_size op 0)
+ *
+ * With dtype GCA_BF16, score_scale must be > 0 (else GCA_ERR_UNSUPPORTED): the
+ * scan prunes candidates on unscaled dot products, whose order is the order of
+ * r only for a positive scale.  GCA_F32 takes any finite scale.
  */
 gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
                         const int32_t* q_pos, int32_t* idx, float* score, float* w,

@@ -284,6 +284,10 @@ static gca_status retrieve_impl(const char* fn, const gca_shape* shape, int nois
                                 void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kRetrieve, &z));
+  // the bf16 scan prunes on unscaled dot products (ordered like r only for a
+  // positive scale); the noisy scan prunes on the perturbed scores themselves
+  if (shape->dtype == GCA_BF16 && noise == 0 && !(shape->score_scale > 0.0f))
+    return fail(GCA_ERR_UNSUPPORTED, "%s: bf16 retrieval needs score_scale > 0", fn);
   if (z.q_rows == 0) {
     g_err[0] = '\0';
     return GCA_OK;

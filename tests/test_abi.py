@@ -108,6 +108,15 @@ def test_retrieve_needs_workspace_when_sliced():
     assert st == 3 and "workspace" in msg
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0, float("-0.0")])
+def test_bf16_retrieve_needs_positive_score_scale(scale):
+    # the bf16 scan prunes on unscaled dot products: rejected before any device call
+    s = _bf16_shape(score_scale=scale)
+    st, msg = _status("gca_retrieve", ctypes.byref(s), A, A, A, A, A, A, A,
+                      ctypes.c_size_t(1 << 30), None)
+    assert st == 2 and "score_scale > 0" in msg
+
+
 def test_backward_rejects_small_workspace_and_missing_landmarks():
     s = _bf16_shape()
     need = gca.gca_workspace_size(s, gca.OP_BACKWARD)
