@@ -221,6 +221,8 @@ gca_status gca_gather_kv(const gca_shape* shape, const int32_t* idx, const void*
  * Supported: dtype GCA_BF16, head_dim 64, T a multiple of 64 (whole 64-token
  * chunks) below 2^30, window >= 1 (any value; windows >= T give causal
  * attention), B*H*T/64 < 2^31.  Same conventions, checks and errors as the GCA calls.
+ * gca_swa_forward needs scale >= 0, as gca_forward does for bf16 (else
+ * GCA_ERR_UNSUPPORTED).
  * gca_swa_backward needs a workspace of gca_swa_workspace_size bytes (D rows).
  */
 typedef struct {
@@ -263,6 +265,10 @@ gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const voi
  *   o     [G, B, H, Nq, S, D]  dtype, big, output
  *   lse   [G, B, H, Nq, k, S]  float32 output, may be NULL (then not written;
  *                              gca_backward needs it)
+ *
+ * With dtype GCA_BF16, attn_scale must be >= 0 (else GCA_ERR_UNSUPPORTED): the
+ * kernel subtracts each row's largest unscaled product before exponentiating,
+ * which bounds the exponents only for a non-negative scale.
  */
 gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
                        const void* v, const int32_t* idx, const float* w, void* o,

@@ -417,6 +417,8 @@ gca_status gca_swa_forward(const gca_swa_shape* shape, const void* q, const void
                            const void* v, void* o, float* lse, void* stream) {
   int64_t heads;
   GCA_TRY(check_swa(shape, &heads));
+  if (shape->scale < 0.0f)  // the row shift is the largest unscaled product, as in gca_forward
+    return fail(GCA_ERR_UNSUPPORTED, "gca_swa_forward: needs scale >= 0");
   if (shape->T == 0) {
     g_err[0] = '\0';
     return GCA_OK;
@@ -491,6 +493,10 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, con
                        const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kForward, &z));
+  // the bf16 kernel shifts by the largest unscaled product: a bound on the
+  // exponents only for a non-negative scale
+  if (shape->dtype == GCA_BF16 && shape->attn_scale < 0.0f)
+    return fail(GCA_ERR_UNSUPPORTED, "gca_forward: bf16 attention needs attn_scale >= 0");
   if (z.q_rows == 0) {
     g_err[0] = '\0';
     return GCA_OK;

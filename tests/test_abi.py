@@ -101,6 +101,16 @@ def test_forward_rejects_null_and_misaligned():
     assert st == 1 and "o is NULL" in msg
 
 
+def test_forwards_need_non_negative_attention_scale():
+    # the bf16 forwards shift rows by the largest unscaled product
+    s = _bf16_shape(attn_scale=-0.125)
+    st, msg = _status("gca_forward", ctypes.byref(s), A, A, A, A, A, A, None, None)
+    assert st == 2 and "attn_scale >= 0" in msg
+    sw = gca.make_swa_shape(2, 3, 1024, 64, 512, scale=-0.125)
+    st, msg = _status("gca_swa_forward", ctypes.byref(sw), A, A, A, A, None, None)
+    assert st == 2 and "scale >= 0" in msg
+
+
 def test_retrieve_needs_workspace_when_sliced():
     s = _bf16_shape(G=1, B=1, n_query=32, n_key=262144, softmax_one=0)
     st, msg = _status("gca_retrieve", ctypes.byref(s), A, A, A, A, A, A, None,
