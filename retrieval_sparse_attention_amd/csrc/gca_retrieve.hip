@@ -640,7 +640,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
                                                    const bf16* __restrict__ lq,
                                                    const bf16* __restrict__ lk, int64_t n_query,
                                                    int64_t n_key, int dl, float score_scale) {
-  __shared__ uint64_t lst[kMergeMax];
+  __shared__ uint64_t lst[MW > 0 ? 64 * MW : kMergeMax];  // packed keys: at most n
   __shared__ uint64_t out[KMAX];
   __shared__ float clean[KMAX];  // with noise: clean scores of the selected
   const int lane = threadIdx.x;
