@@ -161,6 +161,20 @@ def test_gumbel_bf16_long_slices():
     check_gumbel(lq, lk, q_pos.numpy(), k, shape.score_scale, 1, seed, got, True)
 
 
+def test_gumbel_bf16_streamed_merge():
+    # one head over 25500 candidates: 200 slices of one round each, so the merge
+    # takes 1600 partial keys per query, more than fit in registers, and streams them
+    n_query, n_key, k = 20, 25500, 8
+    g = torch.Generator().manual_seed(57)
+    lq = (torch.randn(1, 1, 1, n_query, 64, generator=g) * 0.125).to(torch.bfloat16)
+    lk = (torch.randn(1, 1, 1, n_key, 64, generator=g) * 0.125).to(torch.bfloat16)
+    q_pos = torch.tensor([n_key + 1] * 16 + [20000, 3000, 129, 1], dtype=torch.int32)
+    shape = gca.make_shape(1, 1, 1, n_query, n_key, 64, 64, 64, k, gca.GCA_BF16, 0)
+    seed = 0xBADC0DE
+    got = run_gumbel(shape, seed, dev(lq), dev(lk), dev(q_pos))
+    check_gumbel(lq, lk, q_pos.numpy(), k, shape.score_scale, 0, seed, got, True)
+
+
 def test_gumbel_is_deterministic_and_plan_independent():
     n_query, dl, k = 24, 64, 8
     lq, lk = _sliced_inputs(n_query, 3000, dl, seed=3)
