@@ -67,26 +67,23 @@ __device__ void finalize_query(const float (&s_in)[KMAX], const int (&i_in)[KMAX
   for (int p = 0; p < KMAX; ++p)
     if (p < m) mx = fmaxf(mx, s[p]);
   const float shift = softmax_one ? fmaxf(mx, 0.0f) : mx;
+  // exponentials by the hardware exp2 (a few ulps), one reciprocal of z
   float e[KMAX];
-  float z = softmax_one ? expf(-shift) : 0.0f;
+  float z = softmax_one ? fast_exp2(-shift * kLog2e) : 0.0f;
 #pragma unroll
   for (int p = 0; p < KMAX; ++p) {
-    e[p] = (p < m) ? expf(s[p] - shift) : 0.0f;
+    e[p] = (p < m) ? fast_exp2((s[p] - shift) * kLog2e) : 0.0f;
     z += e[p];
   }
-  for (int p = 0; p < k; ++p) {
-    float sv = 0.0f, wv = 0.0f;
-    int iv = -1;
+  const float rz = 1.0f / z;  // z >= 1 when m > 0 (the largest term is 1)
 #pragma unroll
-    for (int u = 0; u < KMAX; ++u)
-      if (u == p && p < m) {
-        sv = s[u];
-        wv = e[u] / z;
-        iv = id[u];
-      }
-    idx_out[p] = iv;
-    score_out[p] = sv;
-    w_out[p] = wv;
+  for (int p = 0; p < KMAX; ++p) {
+    if (p < k) {
+      const bool ok = p < m;
+      idx_out[p] = ok ? id[p] : -1;
+      score_out[p] = ok ? s[p] : 0.0f;
+      w_out[p] = ok ? e[p] * rz : 0.0f;
+    }
   }
 }
 
