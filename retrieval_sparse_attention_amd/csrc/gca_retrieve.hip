@@ -651,6 +651,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
                                                    int64_t n_key, int dl, float score_scale) {
   __shared__ uint64_t lst[MW > 0 ? 64 * MW : kMergeMax];  // packed keys: at most n
   __shared__ uint64_t out[KMAX];
+  __shared__ __align__(16) uint64_t lane_max[64];
   __shared__ float clean[KMAX];  // with noise: clean scores of the selected
   const int lane = threadIdx.x;
   const int64_t qrow = blockIdx.x;
@@ -683,14 +684,16 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
     }
   }
   // rank of this lane's maximum among the 64 (ties between empty lanes broken
-  // by lane number), then the maximum of rank k-1
+  // by lane number), then the maximum of rank k-1; the 64 maxima go through
+  // LDS once and come back as broadcast reads, all issued together
+  lane_max[lane] = mx;
+  __syncthreads();
   int rank = 0;
 #pragma unroll
-  for (int l = 0; l < 64; ++l) {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mx, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mx >> 32), l);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    rank += (o > mx || (o == mx && l < lane)) ? 1 : 0;
+  for (int l = 0; l < 64; l += 2) {
+    const ulonglong2 o = *(const ulonglong2*)&lane_max[l];
+    rank += (o.x > mx || (o.x == mx && l < lane)) ? 1 : 0;
+    rank += (o.y > mx || (o.y == mx && l + 1 < lane)) ? 1 : 0;
   }
   const uint64_t sel = __ballot(rank == k - 1);
   const int src_lane = __builtin_ctzll(sel);  // k <= 16 < 64: exactly one lane
