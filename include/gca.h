@@ -160,7 +160,8 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
  *   (j / 4, t, (g*B + b)*H + h, 0) and key (seed mod 2^32, seed / 2^32);
  *   the min(k, #candidates) best by (r_j + G_j descending, j ascending) are
  *   selected (r_j + G_j formed as fma(dot, score_scale, G_j) in float32, with
- *   G_j computed in float32 to within about 1e-6 of its exact value);
+ *   G_j computed in float32 to within a few 1e-6 of its exact value: the
+ *   hardware base-2 logarithm is not correctly rounded);
  *   idx holds them in ascending j; score = the clean r_j of each selected
  *   chunk (float32 dot product times score_scale) and w = Eq. 3 over those
  *   clean scores, exactly as in gca_retrieve.  So gradients of w reach r, and

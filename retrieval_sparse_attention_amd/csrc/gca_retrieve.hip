@@ -147,10 +147,11 @@ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32
 // float32, strictly inside (0, 1)), E = -ln U, G = -ln E, with the hardware
 // base-2 logarithm and no library calls.  Above U = 15/16, E comes from
 // t = 1 - U (exact) by the series t + t^2/2 + ... + t^6/6, whose first left-out
-// term is below t^7/7 <= 2^-28 t / 7, so E keeps full relative accuracy near
-// U = 1; below, E = -log2(U) ln 2, where |log2 U| >= 0.09.  Over all 2^23
-// words, E is within 1.3e-7 relative and G within 1.1e-6 absolute of the exact
-// values (with a correctly rounded log2).
+// term is below t^7/7 <= 2^-24 t / 7 (t <= 1/16), so E keeps full relative
+// accuracy near U = 1; below, E = -log2(U) ln 2, where |log2 U| >= 0.09.  Over
+// all 2^23 words, E is within 1.3e-7 relative and G within 1.1e-6 absolute of
+// the exact values if log2 were correctly rounded; v_log_f32 is not (about one
+// ulp), which leaves G within a few 1e-6.
 __device__ __forceinline__ float gumbel_from_word(uint32_t word) {
   constexpr float kLn2 = 0.69314718f;
   const float u = (float)(word >> 9) * 0x1p-23f + 0x1p-24f;
