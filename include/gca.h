@@ -146,6 +146,27 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gca_retrieve_noalloc -- gca_retrieve for callers that cannot allocate.
+ *
+ * For callers that may not call hipMalloc or take a workspace from an
+ * allocator: code under HIP graph capture, tight serving loops (one retrieval
+ * per 64-token chunk step), harnesses that forbid allocation.  Same arguments,
+ * layouts, results and errors as gca_retrieve, without ws / ws_bytes: the
+ * partial top-k lists of a sliced scan go to a scratch array the library owns,
+ * 4 MiB per device (a file-scope device array each GPU holds until the process
+ * ends; its address is looked up once per device).  The call allocates
+ * nothing.  A shape whose gca_workspace_size (op 0) exceeds 4 MiB is refused
+ * with GCA_ERR_UNSUPPORTED before anything is launched (every shape whose
+ * scan is not sliced needs none).  All calls on one GPU share that GPU's
+ * array: two calls that overlap in time on one device (on different streams,
+ * or from different threads) race on it and give undefined results; calls
+ * ordered on one stream do not.
+ */
+gca_status gca_retrieve_noalloc(const gca_shape* shape, const void* lq, const void* lk,
+                                const int32_t* q_pos, int32_t* idx, float* score, float* w,
+                                void* stream);
+
+/*
  * gca_retrieve_gumbel -- gca_retrieve with Gumbel top-k selection (training).
  *
  * Definition: paperlayer.ai summary, section 3.2 (Training & Inference): while

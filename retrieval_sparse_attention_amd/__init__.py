@@ -6,6 +6,7 @@ used for device memory and streams) and enqueue work on torch's current
 stream.  The entry points mirror the C ABI in include/gca.h:
 
   gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None)
+  gca_retrieve_noalloc(shape, lq, lk, q_pos, idx, score, w)     no workspace, no allocation
   gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None)
   gca_gather_kv(shape, idx, k, v, k_packed, v_packed, idx_packed)   k, v may be pinned host
   gca_forward(shape, q, k, v, idx, w, o, lse=None)
@@ -25,7 +26,8 @@ import os
 
 __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library_path",
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
-           "gca_workspace_size", "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv",
+           "gca_workspace_size", "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel",
+           "gca_gather_kv",
            "gca_forward", "gca_backward", "GcaSwaShape", "make_swa_shape",
            "gca_swa_workspace_size", "gca_swa_forward", "gca_swa_backward",
            "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
@@ -36,7 +38,8 @@ GCA_F32 = 0
 GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
-            "gca_retrieve", "gca_retrieve_gumbel", "gca_gather_kv", "gca_forward", "gca_backward",
+            "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel", "gca_gather_kv",
+            "gca_forward", "gca_backward",
             "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
             "gca_swa_forward", "gca_swa_backward")
@@ -106,6 +109,8 @@ def load():
     lib.gca_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.gca_retrieve.restype = ctypes.c_int
     lib.gca_retrieve.argtypes = [sp] + [vp] * 6 + [vp, sz, vp]
+    lib.gca_retrieve_noalloc.restype = ctypes.c_int
+    lib.gca_retrieve_noalloc.argtypes = [sp] + [vp] * 6 + [vp]
     lib.gca_retrieve_gumbel.restype = ctypes.c_int
     lib.gca_retrieve_gumbel.argtypes = [sp, ctypes.c_uint64] + [vp] * 6 + [vp, sz, vp]
     lib.gca_gather_kv.restype = ctypes.c_int
@@ -189,6 +194,12 @@ def gca_retrieve(shape, lq, lk, q_pos, idx, score, w, ws=None):
         ctypes.byref(shape), _ptr(lq, "lq"), _ptr(lk, "lk"), _ptr(q_pos, "q_pos"),
         _ptr(idx, "idx"), _ptr(score, "score"), _ptr(w, "w"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_retrieve_noalloc(shape, lq, lk, q_pos, idx, score, w):
+    _check(load().gca_retrieve_noalloc(
+        ctypes.byref(shape), _ptr(lq, "lq"), _ptr(lk, "lk"), _ptr(q_pos, "q_pos"),
+        _ptr(idx, "idx"), _ptr(score, "score"), _ptr(w, "w"), _stream()))
 
 
 def gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None):

@@ -341,6 +341,28 @@ gca_status gca_retrieve(const gca_shape* shape, const void* lq, const void* lk,
                        stream);
 }
 
+gca_status gca_retrieve_noalloc(const gca_shape* shape, const void* lq, const void* lk,
+                                const int32_t* q_pos, int32_t* idx, float* score, float* w,
+                                void* stream) {
+  Sizes z;
+  GCA_TRY(check_shape(shape, kRetrieve, &z));
+  const size_t need_bytes = retrieve_ws(shape, z, plan_scan(shape, z)).total;
+  if (need_bytes > gca::kScratchBytes)
+    return fail(GCA_ERR_UNSUPPORTED,
+                "gca_retrieve_noalloc: this shape needs %zu scratch bytes, more than the "
+                "library's %zu; call gca_retrieve with a workspace",
+                need_bytes, gca::kScratchBytes);
+  void* ws = nullptr;
+  if (need_bytes > 0) {
+    const hipError_t e = gca::scratch_address(&ws);
+    if (e != hipSuccess)
+      return fail(GCA_ERR_DEVICE, "gca_retrieve_noalloc: scratch address: %s (%s)",
+                  hipGetErrorName(e), hipGetErrorString(e));
+  }
+  return retrieve_impl("gca_retrieve_noalloc", shape, 0, 0, lq, lk, q_pos, idx, score, w, ws,
+                       need_bytes > 0 ? gca::kScratchBytes : 0, stream);
+}
+
 gca_status gca_retrieve_gumbel(const gca_shape* shape, uint64_t seed, const void* lq,
                                const void* lk, const int32_t* q_pos, int32_t* idx, float* score,
                                float* w, void* ws, size_t ws_bytes, void* stream) {

@@ -136,6 +136,12 @@ class KernelTimer {
   hipEvent_t start_ = nullptr;
 };
 
+// Size of the library-owned scratch array gca_retrieve_noalloc uses in place
+// of a workspace (one per device), and its device address on the current
+// device (looked up once per device and kept).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+hipError_t scratch_address(void** ptr);
+
 hipError_t launch_retrieve(const ScanPlan& plan, const LaunchRetrieve& a);
 hipError_t launch_forward(const LaunchForward& a);
 hipError_t launch_backward(const LaunchBackward& a);
