@@ -492,6 +492,24 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
   }
 }
 
+// Order in which key chunks go out: chunk-major within groups of kKvHeadGroup
+// consecutive heads (chunk 0 of each head in the group, then chunk 1, ...).
+// A chunk's work grows with its reverse list, and in causal training the
+// early chunks collect the longest lists (about k ln(n/c) entries for chunk
+// c): head after head, the last heads' long lists would start only near the
+// end of the grid and run alone.  Mixing a few heads puts every long list
+// early while the Q/dO tiles in use stay those of a few heads (each XCD works
+// through one contiguous range of this order, see xcd_tile).
+constexpr int64_t kKvHeadGroup = 3;
+
+__device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64_t heads) {
+  const int64_t per = kKvHeadGroup * n_key;
+  const int64_t grp = i / per, within = i % per;
+  const int64_t h0 = grp * kKvHeadGroup;
+  const int64_t gh = heads - h0 < kKvHeadGroup ? heads - h0 : kKvHeadGroup;
+  return (h0 + within % gh) * n_key + within / gh;
+}
+
 __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
@@ -507,7 +525,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
   __shared__ int s_ent[256];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
-  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_key + c
+  // = head * n_key + c
+  const int64_t tile = kv_tile_order(xcd_tile(blockIdx.x, gridDim.x), n_key, gridDim.x / n_key);
   const int64_t head = tile / n_key;
   const int64_t c = tile % n_key;
   const int j = 16 * wave + col;  // key row owned by this lane
