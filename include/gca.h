@@ -21,8 +21,9 @@
  *   gca_swa_forward / gca_swa_backward -- the layer's causal sliding-window
  *                          self-attention
  * An upper layer group reuses one gca_retrieve (and one K/V) for all of its
- * layers: each layer calls gca_forward / gca_backward with the same idx, w, K
- * and V, and the shared tensors' gradients are the sums over the layers.
+ * layers: each layer calls gca_forward, then gca_backward_accumulate, with the
+ * same idx, w, K and V; the library adds every layer's gradients of the shared
+ * tensors into float32 accumulators.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -49,7 +50,11 @@
  *   synchronise its stream and check for device errors before returning.
  *
  * Supported sizes (anything else returns GCA_ERR_UNSUPPORTED):
- *   dtype GCA_BF16 : chunk_size 64, head_dim 64, landmark_dim 32 or 64
+ *   dtype GCA_BF16 : chunk_size 1..64, head_dim 1..64, landmark_dim 32 or 64
+ *                    (gca_forward / gca_backward run MFMA kernels at
+ *                    chunk_size = head_dim = 64, the pages' chunk size; other
+ *                    sizes, e.g. S = 16 or D = 32, take a float32 VALU path
+ *                    with bf16 loads and one rounding of each output)
  *   dtype GCA_F32  : chunk_size 1..64, head_dim 1..64, landmark_dim 1..128
  *   top_k 1..16; n_key < 2^31 - 1; at most 2^31 - 1 query or key chunk tiles
  *   (G*B*H*n_query, G*B*H*n_key); gca_backward needs n_query * top_k < 2^31.
@@ -289,9 +294,10 @@ gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const voi
  *   lse   [G, B, H, Nq, k, S]  float32 output, may be NULL (then not written;
  *                              gca_backward needs it)
  *
- * With dtype GCA_BF16, attn_scale must be >= 0 (else GCA_ERR_UNSUPPORTED): the
- * kernel subtracts each row's largest unscaled product before exponentiating,
- * which bounds the exponents only for a non-negative scale.
+ * With dtype GCA_BF16 and chunk_size = head_dim = 64, attn_scale must be >= 0
+ * (else GCA_ERR_UNSUPPORTED): that kernel subtracts each row's largest unscaled
+ * product before exponentiating, which bounds the exponents only for a
+ * non-negative scale.
  */
 gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
                        const void* v, const int32_t* idx, const float* w, void* o,
@@ -342,6 +348,38 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k,
                         const void* lk, void* dq, void* dk, void* dv, float* dw,
                         float* dscore, float* dlq, float* dlk, void* ws,
                         size_t ws_bytes, void* stream);
+
+/*
+ * gca_backward_accumulate -- gca_backward for the upper layers of a group that
+ * share one retrieval and one K/V, summing the shared gradients in the library.
+ *
+ * Definition: paperlayer.ai summary, section 3.1 (the retrieved chunks'
+ * representations, and the key/value transformations, are shared across the
+ * upper layers of a group); paperhub.cn review page, authors' reply "Q2" (the
+ * GCA K/V is shared within a group).  Each upper layer l brings its own
+ * queries q_l and upstream gradient dO_l and attends with the same idx, w, K,
+ * V; the loss is a sum over layers, so the gradients of the shared tensors
+ * are the sums over layers of gca_backward's per-layer values.
+ *
+ * Same arguments, checks, workspace (gca_workspace_size op 2) and errors as
+ * gca_backward, with these outputs:
+ *   dq          [G, B, H, Nq, S, D]  dtype, big: this layer's dQ (overwritten)
+ *   dk_acc, dv_acc [G, B, H, Nk, S, D] float32, big: dK, dV of this layer
+ *               are ADDED (float32, before any rounding)
+ *   dw_acc, dscore_acc [G, B, H, Nq, k] float32: dw, dscore ADDED
+ *   dlq_acc [G, B, H, Nq, Dl], dlk_acc [G, B, H, Nk, Dl] float32 or NULL: ADDED
+ * The caller zeroes the accumulators before the first layer and calls once per
+ * layer on one stream; each element's sum then runs over the layers in call
+ * order, and each layer's own terms in gca_backward's fixed order, so results
+ * are bitwise reproducible.  Rounding the float32 sums (e.g. to bf16) is the
+ * caller's.
+ */
+gca_status gca_backward_accumulate(const gca_shape* shape, const void* q, const void* k,
+                                   const void* v, const int32_t* idx, const float* w,
+                                   const float* lse, const void* dout, const void* lq,
+                                   const void* lk, void* dq, float* dk_acc, float* dv_acc,
+                                   float* dw_acc, float* dscore_acc, float* dlq_acc,
+                                   float* dlk_acc, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Per-kernel timing with HIP events (benchmarks, profiling).

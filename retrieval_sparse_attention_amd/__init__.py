@@ -12,6 +12,8 @@ stream.  The entry points mirror the C ABI in include/gca.h:
   gca_forward(shape, q, k, v, idx, w, o, lse=None)
   gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
                dlq=None, dlk=None, ws=None)
+  gca_backward_accumulate(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk_acc, dv_acc,
+               dw_acc, dscore_acc, dlq_acc=None, dlk_acc=None, ws=None)   float32 sums
   gca_workspace_size(shape, op)          op: 0 retrieve, 1 forward, 2 backward
   gca_swa_forward(swa_shape, q, k, v, o, lse=None)      sliding-window self-attention
   gca_swa_backward(swa_shape, q, k, v, o, lse, dout, dq, dk, dv, ws=None)
@@ -28,7 +30,8 @@ __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
            "gca_workspace_size", "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel",
            "gca_gather_kv",
-           "gca_forward", "gca_backward", "GcaSwaShape", "make_swa_shape",
+           "gca_forward", "gca_backward", "gca_backward_accumulate", "GcaSwaShape",
+           "make_swa_shape",
            "gca_swa_workspace_size", "gca_swa_forward", "gca_swa_backward",
            "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
            "EXPORTED", "gca_num_kernels", "gca_kernel_name", "gca_timing_enable",
@@ -39,7 +42,7 @@ GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
             "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel", "gca_gather_kv",
-            "gca_forward", "gca_backward",
+            "gca_forward", "gca_backward", "gca_backward_accumulate",
             "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
             "gca_swa_forward", "gca_swa_backward")
@@ -119,6 +122,8 @@ def load():
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
     lib.gca_backward.restype = ctypes.c_int
     lib.gca_backward.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
+    lib.gca_backward_accumulate.restype = ctypes.c_int
+    lib.gca_backward_accumulate.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
     swp = ctypes.POINTER(GcaSwaShape)
     lib.gca_swa_workspace_size.restype = ctypes.c_int
     lib.gca_swa_workspace_size.argtypes = [swp, ctypes.POINTER(sz)]
@@ -244,6 +249,22 @@ def gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dsco
         _ptr(dq, "dq"), _ptr(dk, "dk"), _ptr(dv, "dv"), _ptr(dw, "dw"), _ptr(dscore, "dscore"),
         _ptr(dlq, "dlq"), _ptr(dlk, "dlk"), _ptr(ws, "ws"),
         ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
+
+
+def gca_backward_accumulate(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk_acc, dv_acc,
+                            dw_acc, dscore_acc, dlq_acc=None, dlk_acc=None, ws=None):
+    for name, t in (("dk_acc", dk_acc), ("dv_acc", dv_acc), ("dw_acc", dw_acc),
+                    ("dscore_acc", dscore_acc), ("dlq_acc", dlq_acc), ("dlk_acc", dlk_acc)):
+        if t is not None and t.dtype != __import__("torch").float32:
+            raise ValueError(f"{name} must be float32")
+    ws = _workspace(shape, OP_BACKWARD, ws, q)
+    _check(load().gca_backward_accumulate(
+        ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(idx, "idx"),
+        _ptr(w, "w"), _ptr(lse, "lse"), _ptr(dout, "dout"), _ptr(lq, "lq"), _ptr(lk, "lk"),
+        _ptr(dq, "dq"), _ptr(dk_acc, "dk_acc"), _ptr(dv_acc, "dv_acc"), _ptr(dw_acc, "dw_acc"),
+        _ptr(dscore_acc, "dscore_acc"), _ptr(dlq_acc, "dlq_acc"), _ptr(dlk_acc, "dlk_acc"),
+        _ptr(ws, "ws"), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+        _stream()))
 
 
 def gca_swa_workspace_size(shape):

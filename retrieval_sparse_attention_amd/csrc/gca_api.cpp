@@ -79,8 +79,8 @@ gca_status check_shape(const gca_shape* s, int op, Sizes* z) {
   if (!std::isfinite(s->attn_scale) || !std::isfinite(s->score_scale))
     return fail(GCA_ERR_INVALID_ARGUMENT, "attn_scale and score_scale must be finite");
   if (s->dtype == GCA_BF16) {
-    if (op != kRetrieve && (s->chunk_size != 64 || s->head_dim != 64))
-      return fail(GCA_ERR_UNSUPPORTED, "bf16 attention needs chunk_size = head_dim = 64");
+    if (op != kRetrieve && (s->chunk_size > 64 || s->head_dim > 64))
+      return fail(GCA_ERR_UNSUPPORTED, "bf16 attention needs chunk_size, head_dim <= 64");
     if (op != kForward && s->landmark_dim != 32 && s->landmark_dim != 64)
       return fail(GCA_ERR_UNSUPPORTED, "bf16 landmarks need landmark_dim 32 or 64");
   } else {
@@ -153,7 +153,7 @@ RetrieveWs retrieve_ws(const gca_shape* s, const Sizes& z, const gca::ScanPlan& 
 }
 
 struct BackwardWs {
-  size_t delta, rev_off, rev_ent, total;
+  size_t delta, rev_off, rev_ent, ds_layer, total;
 };
 
 BackwardWs backward_ws(const gca_shape* s, const Sizes& z) {
@@ -161,7 +161,8 @@ BackwardWs backward_ws(const gca_shape* s, const Sizes& z) {
   w.delta = 0;
   w.rev_off = align_up((size_t)z.slots * (size_t)s->chunk_size * sizeof(float));
   w.rev_ent = w.rev_off + align_up((size_t)z.heads * (size_t)(s->n_key + 1) * sizeof(int32_t));
-  w.total = w.rev_ent + align_up((size_t)z.slots * sizeof(int32_t));
+  w.ds_layer = w.rev_ent + align_up((size_t)z.slots * sizeof(int32_t));
+  w.total = w.ds_layer + align_up((size_t)z.slots * sizeof(float));
   return w;
 }
 
@@ -515,10 +516,12 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, con
                        const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kForward, &z));
-  // the bf16 kernel shifts by the largest unscaled product: a bound on the
-  // exponents only for a non-negative scale
-  if (shape->dtype == GCA_BF16 && shape->attn_scale < 0.0f)
-    return fail(GCA_ERR_UNSUPPORTED, "gca_forward: bf16 attention needs attn_scale >= 0");
+  // the bf16 MFMA kernel (64 x 64 tiles) shifts by the largest unscaled
+  // product: a bound on the exponents only for a non-negative scale
+  if (shape->dtype == GCA_BF16 && shape->chunk_size == 64 && shape->head_dim == 64 &&
+      shape->attn_scale < 0.0f)
+    return fail(GCA_ERR_UNSUPPORTED,
+                "gca_forward: bf16 attention on 64 x 64 tiles needs attn_scale >= 0");
   if (z.q_rows == 0) {
     g_err[0] = '\0';
     return GCA_OK;
@@ -554,11 +557,12 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, con
   return device_status(gca::launch_forward(a), a.stream, "gca_forward");
 }
 
-gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, const void* v,
-                        const int32_t* idx, const float* w, const float* lse, const void* dout,
-                        const void* lq, const void* lk, void* dq, void* dk, void* dv, float* dw,
-                        float* dscore, float* dlq, float* dlk, void* ws, size_t ws_bytes,
-                        void* stream) {
+static gca_status backward_impl(const char* fn, int accumulate, const gca_shape* shape,
+                                const void* q, const void* k, const void* v, const int32_t* idx,
+                                const float* w, const float* lse, const void* dout,
+                                const void* lq, const void* lk, void* dq, void* dk, void* dv,
+                                float* dw, float* dscore, float* dlq, float* dlk, void* ws,
+                                size_t ws_bytes, void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kBackward, &z));
   if (z.q_rows == 0 && z.k_rows == 0) {
@@ -572,17 +576,17 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
     GCA_TRY(need(w, "w", 4));
     GCA_TRY(need(lse, "lse", 4));
     GCA_TRY(need(dq, "dq", 16));
-    GCA_TRY(need(dw, "dw", 4));
-    GCA_TRY(need(dscore, "dscore", 4));
+    GCA_TRY(need(dw, accumulate ? "dw_acc" : "dw", 4));
+    GCA_TRY(need(dscore, accumulate ? "dscore_acc" : "dscore", 4));
   }
   if (z.k_rows > 0) {
     GCA_TRY(need(k, "k", 16));
     GCA_TRY(need(v, "v", 16));
-    GCA_TRY(need(dk, "dk", 16));
-    GCA_TRY(need(dv, "dv", 16));
+    GCA_TRY(need(dk, accumulate ? "dk_acc" : "dk", 16));
+    GCA_TRY(need(dv, accumulate ? "dv_acc" : "dv", 16));
   }
-  GCA_TRY(opt(dlq, "dlq", 4));
-  GCA_TRY(opt(dlk, "dlk", 4));
+  GCA_TRY(opt(dlq, accumulate ? "dlq_acc" : "dlq", 4));
+  GCA_TRY(opt(dlk, accumulate ? "dlk_acc" : "dlk", 4));
   // dlq sums over retrieved chunks' landmarks: with no resident chunk it is 0
   if (dlq != nullptr && z.q_rows > 0 && shape->n_key > 0)
     GCA_TRY(need(lk, "lk (needed for dlq)", 16));
@@ -591,7 +595,7 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
   GCA_TRY(opt(lk, "lk", 16));
   const BackwardWs wl = backward_ws(shape, z);
   if (ws == nullptr || ws_bytes < wl.total)
-    return fail(GCA_ERR_WORKSPACE, "gca_backward needs %zu workspace bytes, got %zu", wl.total,
+    return fail(GCA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", fn, wl.total,
                 ws == nullptr ? (size_t)0 : ws_bytes);
   if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
   gca::LaunchBackward a{};
@@ -623,9 +627,11 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
   a.dscore = dscore;
   a.dlq = dlq;
   a.dlk = dlk;
+  a.accumulate = accumulate;
   a.delta = (float*)((char*)ws + wl.delta);
   a.rev_off = (int32_t*)((char*)ws + wl.rev_off);
   a.rev_ent = (int32_t*)((char*)ws + wl.rev_ent);
+  a.ds_layer = (float*)((char*)ws + wl.ds_layer);
   a.stream = (hipStream_t)stream;
   std::lock_guard<std::mutex> lock(g_side_mu);
   if (SideResources* sr = side_resources()) {
@@ -633,7 +639,27 @@ gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, co
     a.fork = sr->fork;
     a.join = sr->join;
   }
-  return device_status(gca::launch_backward(a), a.stream, "gca_backward");
+  return device_status(gca::launch_backward(a), a.stream, fn);
+}
+
+gca_status gca_backward(const gca_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const float* w, const float* lse, const void* dout,
+                        const void* lq, const void* lk, void* dq, void* dk, void* dv, float* dw,
+                        float* dscore, float* dlq, float* dlk, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return backward_impl("gca_backward", 0, shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv,
+                       dw, dscore, dlq, dlk, ws, ws_bytes, stream);
+}
+
+gca_status gca_backward_accumulate(const gca_shape* shape, const void* q, const void* k,
+                                   const void* v, const int32_t* idx, const float* w,
+                                   const float* lse, const void* dout, const void* lq,
+                                   const void* lk, void* dq, float* dk_acc, float* dv_acc,
+                                   float* dw_acc, float* dscore_acc, float* dlq_acc,
+                                   float* dlk_acc, void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl("gca_backward_accumulate", 1, shape, q, k, v, idx, w, lse, dout, lq, lk,
+                       dq, dk_acc, dv_acc, dw_acc, dscore_acc, dlq_acc, dlk_acc, ws, ws_bytes,
+                       stream);
 }
 
 }  // extern "C"

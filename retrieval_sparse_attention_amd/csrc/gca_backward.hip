@@ -136,12 +136,22 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
 }
 
 // Score / landmark epilogue of one query chunk, run by the whole workgroup.
-// dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq.  With
-// no resident chunk (lk_head null) every slot is empty and dlq is 0.
-template <typename LT>
+// dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq (ACC:
+// adds them to the float32 accumulators instead).  With no resident chunk
+// (lk_head null) every slot is empty and dlq is 0.
+template <bool ACC>
+__device__ __forceinline__ void put(float* p, float v) {
+  if (ACC)
+    *p += v;
+  else
+    *p = v;
+}
+
+template <typename LT, bool ACC>
 __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_c,
                                const float* wv, float* dw_slot, float* ds_slot,
                                float* __restrict__ dw_out, float* __restrict__ dscore_out,
+                               float* __restrict__ ds_layer,
                                const LT* __restrict__ lk_head, float* __restrict__ dlq_row,
                                int dl, float score_scale) {
   if (tid == 0) {
@@ -151,13 +161,15 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
     for (int i = 0; i < topk; ++i) {
       const bool ok = slot_c[i] >= 0;
       ds_slot[i] = ok ? wv[i] * (dw_slot[i] - sw) : 0.0f;
-      dw_out[i] = ok ? dw_slot[i] : 0.0f;
-      dscore_out[i] = ds_slot[i];
+      put<ACC>(dw_out + i, ok ? dw_slot[i] : 0.0f);
+      put<ACC>(dscore_out + i, ds_slot[i]);
+      if (ACC) ds_layer[i] = ds_slot[i];  // this layer's dscore, for the key side
     }
   }
   __syncthreads();
   if (dlq_row && !lk_head) {
-    for (int d = tid; d < dl; d += nthreads) dlq_row[d] = 0.0f;
+    if (!ACC)
+      for (int d = tid; d < dl; d += nthreads) dlq_row[d] = 0.0f;
   } else if (dlq_row) {
     for (int d = tid; d < dl; d += nthreads) {
       float acc = 0.0f;
@@ -168,7 +180,7 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
         const int c = slot_c[i] >= 0 ? slot_c[i] : 0;
         acc = fmaf(ds_slot[i], load_f(lk_head + (int64_t)c * dl + d), acc);
       }
-      dlq_row[d] = score_scale * acc;
+      put<ACC>(dlq_row + d, score_scale * acc);
     }
   }
 }
@@ -272,13 +284,14 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
   }
 }
 
+template <bool ACC>
 __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
     const bf16* __restrict__ dout, const bf16* __restrict__ lk, bf16* __restrict__ dq,
     float* __restrict__ dw_out, float* __restrict__ dscore_out, float* __restrict__ dlq,
-    float* __restrict__ delta, int64_t n_query, int64_t n_key, int topk, int dl,
-    float attn_scale, float score_scale) {
+    float* __restrict__ delta, float* __restrict__ ds_layer, int64_t n_query, int64_t n_key,
+    int topk, int dl, float attn_scale, float score_scale) {
   __shared__ __align__(16) bf16 k_lds[2][kTileElems];
   __shared__ __align__(16) bf16 v_lds[2][kTileElems];
   __shared__ float dw_part[4][16];
@@ -369,8 +382,9 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   for (int e = tid; e < topk * 64; e += 256) delta[tile * topk * 64 + e] = s_delta[e];
   if (tid < topk) dw_slot[tid] = (dw_part[0][tid] + dw_part[1][tid]) + (dw_part[2][tid] + dw_part[3][tid]);
   __syncthreads();
-  score_epilogue<bf16>(tid, 256, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
-                       dscore_out + tile * topk, lk ? lk + head * n_key * dl : nullptr,
+  score_epilogue<bf16, ACC>(tid, 256, topk, slot_c, slot_w, dw_slot, ds_slot,
+                            dw_out + tile * topk, dscore_out + tile * topk,
+                            ACC ? ds_layer + tile * topk : nullptr, lk ? lk + head * n_key * dl : nullptr,
                        dlq ? dlq + tile * dl : nullptr, dl, score_scale);
 }
 
@@ -510,12 +524,15 @@ __device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64
   return (h0 + within % gh) * n_key + within / gh;
 }
 
+// ACC: dk and dv are float32 accumulators that this layer's gradients are
+// added to (in place of bf16 outputs), dlk likewise.
+template <bool ACC>
 __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
     const int32_t* __restrict__ rev_ent, const bf16* __restrict__ lq,
-    const float* __restrict__ dscore, bf16* __restrict__ dk, bf16* __restrict__ dv,
+    const float* __restrict__ dscore, void* __restrict__ dk, void* __restrict__ dv,
     float* __restrict__ dlk, int64_t n_query, int64_t n_key, int topk, int dl,
     float attn_scale, float score_scale) {
   __shared__ __align__(16) bf16 q_lds[2][kTileElems];
@@ -582,32 +599,57 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
                     l2_lds[1], d_lds[1], q_lds[0], do_lds[0]);
     }
   }
-  bf16* dkrow = dk + tile * 4096 + j * 64 + 4 * grp;
-  bf16* dvrow = dv + tile * 4096 + j * 64 + 4 * grp;
+  const int64_t orow = tile * 4096 + j * 64 + 4 * grp;
+  if (ACC) {
+    f32x4* dka = (f32x4*)((float*)dk + orow);
+    f32x4* dva = (f32x4*)((float*)dv + orow);
+    f32x4 ka[4], va[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    bf16x4 kv4, vv4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kv4[e] = (bf16)(attn_scale * dkacc[dt][e]);
-      vv4[e] = (bf16)dvacc[dt][e];
+    for (int dt = 0; dt < 4; ++dt) {
+      ka[dt] = dka[4 * dt];
+      va[dt] = dva[4 * dt];
     }
-    *(bf16x4*)(dkrow + 16 * dt) = kv4;
-    *(bf16x4*)(dvrow + 16 * dt) = vv4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ka[dt][e] += attn_scale * dkacc[dt][e];
+        va[dt][e] += dvacc[dt][e];
+      }
+      dka[4 * dt] = ka[dt];
+      dva[4 * dt] = va[dt];
+    }
+  } else {
+    bf16* dkrow = (bf16*)dk + orow;
+    bf16* dvrow = (bf16*)dv + orow;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      bf16x4 kv4, vv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv4[e] = (bf16)(attn_scale * dkacc[dt][e]);
+        vv4[e] = (bf16)dvacc[dt][e];
+      }
+      *(bf16x4*)(dkrow + 16 * dt) = kv4;
+      *(bf16x4*)(dvrow + 16 * dt) = vv4;
+    }
   }
-  if (dlk && tid < dl) dlk[tile * dl + tid] = score_scale * dlk_acc;
+  if (dlk && tid < dl) put<ACC>(dlk + tile * dl + tid, score_scale * dlk_acc);
 }
 
 // ---------------------------------------------------------------------------
-// float32 query-side backward: 64 threads per query chunk, thread x owns row x.
+// Generic query-side backward (any S, D <= 64; float32 or bf16 elements): 64
+// threads per query chunk, thread x owns row x; float32 arithmetic, dQ
+// accumulated in registers and rounded to the element type once.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_bwd_q_f32(
-    const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
+template <typename T, bool ACC>
+__global__ __launch_bounds__(64) void k_bwd_q_gen(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
-    const float* __restrict__ dout, const float* __restrict__ lk, float* __restrict__ dq,
+    const T* __restrict__ dout, const T* __restrict__ lk, T* __restrict__ dq,
     float* __restrict__ dw_out, float* __restrict__ dscore_out, float* __restrict__ dlq,
-    float* __restrict__ delta, int64_t n_query, int64_t n_key, int S, int D, int topk, int dl,
-    float attn_scale, float score_scale) {
+    float* __restrict__ delta, float* __restrict__ ds_layer, int64_t n_query, int64_t n_key,
+    int S, int D, int topk, int dl, float attn_scale, float score_scale) {
   __shared__ float kt[64 * 64];
   __shared__ float vt[64 * 64];
   __shared__ float pr[64 * 65];
@@ -620,16 +662,16 @@ __global__ __launch_bounds__(64) void k_bwd_q_f32(
   const int64_t tile = blockIdx.x;
   const int64_t head = tile / n_query;
   const int64_t tsz = (int64_t)S * D;
-  const float* qrow = q + tile * tsz + (int64_t)x * D;
-  const float* dorow = dout + tile * tsz + (int64_t)x * D;
-  float* dqrow = dq + tile * tsz + (int64_t)x * D;
+  const T* qrow = q + tile * tsz + (int64_t)x * D;
+  const T* dorow = dout + tile * tsz + (int64_t)x * D;
   if (x < topk) {
     const int c = idx[tile * topk + x];
     slot_c[x] = (c >= 0 && c < n_key) ? c : -1;
     slot_w[x] = w[tile * topk + x];
   }
-  if (x < S)
-    for (int d = 0; d < D; ++d) dqrow[d] = 0.0f;
+  float dqa[64];
+#pragma unroll
+  for (int d = 0; d < 64; ++d) dqa[d] = 0.0f;
   __syncthreads();
   for (int i = 0; i < topk; ++i) {
     const int c = slot_c[i];
@@ -641,11 +683,11 @@ __global__ __launch_bounds__(64) void k_bwd_q_f32(
     }
     const float wi = slot_w[i];
     __syncthreads();
-    const float* ks = kk + (head * n_key + c) * tsz;
-    const float* vs = v + (head * n_key + c) * tsz;
+    const T* ks = kk + (head * n_key + c) * tsz;
+    const T* vs = v + (head * n_key + c) * tsz;
     for (int e = x; e < S * D; e += 64) {
-      kt[e] = ks[e];
-      vt[e] = vs[e];
+      kt[e] = load_f(ks + e);
+      vt[e] = load_f(vs + e);
     }
     __syncthreads();
     float dsum = 0.0f;
@@ -653,25 +695,28 @@ __global__ __launch_bounds__(64) void k_bwd_q_f32(
       float* p = pr + x * 65;
       const float lx = lse[(tile * topk + i) * S + x];
       for (int jj = 0; jj < S; ++jj) {
-        float s = 0.0f, dp = 0.0f;
+        float sv = 0.0f, dp = 0.0f;
         for (int d = 0; d < D; ++d) {
-          s = fmaf(qrow[d], kt[jj * D + d], s);
-          dp = fmaf(dorow[d], vt[jj * D + d], dp);
+          sv = fmaf(load_f(qrow + d), kt[jj * D + d], sv);
+          dp = fmaf(load_f(dorow + d), vt[jj * D + d], dp);
         }
-        const float pj = expf(s * attn_scale - lx);
+        const float pj = expf(sv * attn_scale - lx);
         p[jj] = pj;
         dsum = fmaf(pj, dp, dsum);
       }
       drow[x] = dsum;
       for (int jj = 0; jj < S; ++jj) {
         float dp = 0.0f;
-        for (int d = 0; d < D; ++d) dp = fmaf(dorow[d], vt[jj * D + d], dp);
+        for (int d = 0; d < D; ++d) dp = fmaf(load_f(dorow + d), vt[jj * D + d], dp);
         p[jj] = wi * p[jj] * (dp - dsum);
       }
-      for (int d = 0; d < D; ++d) {
-        float acc = 0.0f;
-        for (int jj = 0; jj < S; ++jj) acc = fmaf(p[jj], kt[jj * D + d], acc);
-        dqrow[d] += attn_scale * acc;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) {
+        if (d < D) {
+          float acc = 0.0f;
+          for (int jj = 0; jj < S; ++jj) acc = fmaf(p[jj], kt[jj * D + d], acc);
+          dqa[d] = fmaf(attn_scale, acc, dqa[d]);
+        }
       }
     }
     red[x] = (x < S) ? dsum : 0.0f;
@@ -682,21 +727,31 @@ __global__ __launch_bounds__(64) void k_bwd_q_f32(
       dw_slot[i] = t;
     }
   }
+  if (x < S) {
+    T* dqrow = dq + tile * tsz + (int64_t)x * D;
+#pragma unroll
+    for (int d = 0; d < 64; ++d)
+      if (d < D) store_f(dqrow + d, dqa[d]);
+  }
   __syncthreads();
-  score_epilogue<float>(x, 64, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
-                        dscore_out + tile * topk, lk ? lk + head * n_key * dl : nullptr,
-                        dlq ? dlq + tile * dl : nullptr, dl, score_scale);
+  score_epilogue<T, ACC>(x, 64, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
+                         dscore_out + tile * topk, ACC ? ds_layer + tile * topk : nullptr,
+                         lk ? lk + head * n_key * dl : nullptr, dlq ? dlq + tile * dl : nullptr,
+                         dl, score_scale);
 }
 
 // ---------------------------------------------------------------------------
-// float32 key-side backward: 64 threads per key chunk, thread j owns row j.
+// Generic key-side backward (any S, D <= 64; float32 or bf16 elements): 64
+// threads per key chunk, thread j owns row j; dK and dV accumulated in
+// registers (ACC: on top of the float32 accumulators) and stored once.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_bwd_kv_f32(
-    const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
-    const float* __restrict__ w, const float* __restrict__ lse, const float* __restrict__ dout,
+template <typename T, bool ACC>
+__global__ __launch_bounds__(64) void k_bwd_kv_gen(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ v,
+    const float* __restrict__ w, const float* __restrict__ lse, const T* __restrict__ dout,
     const float* __restrict__ delta, const int32_t* __restrict__ rev_off,
-    const int32_t* __restrict__ rev_ent, const float* __restrict__ lq,
-    const float* __restrict__ dscore, float* __restrict__ dk, float* __restrict__ dv,
+    const int32_t* __restrict__ rev_ent, const T* __restrict__ lq,
+    const float* __restrict__ dscore, void* __restrict__ dk, void* __restrict__ dv,
     float* __restrict__ dlk, int64_t n_query, int64_t n_key, int S, int D, int topk, int dl,
     float attn_scale, float score_scale) {
   __shared__ float qt[64 * 64];
@@ -708,15 +763,17 @@ __global__ __launch_bounds__(64) void k_bwd_kv_f32(
   const int64_t head = tile / n_key;
   const int64_t c = tile % n_key;
   const int64_t tsz = (int64_t)S * D;
-  const float* krow = kk + tile * tsz + (int64_t)jj * D;
-  const float* vrow = v + tile * tsz + (int64_t)jj * D;
-  float* dkrow = dk + tile * tsz + (int64_t)jj * D;
-  float* dvrow = dv + tile * tsz + (int64_t)jj * D;
-  if (jj < S)
-    for (int d = 0; d < D; ++d) {
-      dkrow[d] = 0.0f;
-      dvrow[d] = 0.0f;
-    }
+  const T* krow = kk + tile * tsz + (int64_t)jj * D;
+  const T* vrow = v + tile * tsz + (int64_t)jj * D;
+  // ACC: dk, dv are float32 accumulators; else element-type outputs
+  float* dka_out = ACC ? (float*)dk + tile * tsz + (int64_t)jj * D : nullptr;
+  float* dva_out = ACC ? (float*)dv + tile * tsz + (int64_t)jj * D : nullptr;
+  float dka[64], dva[64];
+#pragma unroll
+  for (int d = 0; d < 64; ++d) {
+    dka[d] = (ACC && jj < S && d < D) ? dka_out[d] : 0.0f;
+    dva[d] = (ACC && jj < S && d < D) ? dva_out[d] : 0.0f;
+  }
   float dlk_acc[2] = {0.0f, 0.0f};  // dl <= 128: thread covers d = jj and jj + 64
   const int beg = rev_off[head * (n_key + 1) + c];
   const int end = rev_off[head * (n_key + 1) + c + 1];
@@ -727,11 +784,11 @@ __global__ __launch_bounds__(64) void k_bwd_kv_f32(
     const int64_t pair = head * n_query * topk + ent;
     const float wi = w[pair];
     __syncthreads();
-    const float* qs = q + (head * n_query + t) * tsz;
-    const float* ds = dout + (head * n_query + t) * tsz;
+    const T* qs = q + (head * n_query + t) * tsz;
+    const T* ds = dout + (head * n_query + t) * tsz;
     for (int u = jj; u < S * D; u += 64) {
-      qt[u] = qs[u];
-      dot[u] = ds[u];
+      qt[u] = load_f(qs + u);
+      dot[u] = load_f(ds + u);
     }
     if (jj < S) {
       lx[jj] = lse[pair * S + jj];
@@ -739,31 +796,81 @@ __global__ __launch_bounds__(64) void k_bwd_kv_f32(
     }
     if (lq) {
       const float dsc = dscore[pair];
-      const float* lqr = lq + (head * n_query + t) * dl;
-      if (jj < dl) dlk_acc[0] = fmaf(dsc, lqr[jj], dlk_acc[0]);
-      if (jj + 64 < dl) dlk_acc[1] = fmaf(dsc, lqr[jj + 64], dlk_acc[1]);
+      const T* lqr = lq + (head * n_query + t) * dl;
+      if (jj < dl) dlk_acc[0] = fmaf(dsc, load_f(lqr + jj), dlk_acc[0]);
+      if (jj + 64 < dl) dlk_acc[1] = fmaf(dsc, load_f(lqr + jj + 64), dlk_acc[1]);
     }
     __syncthreads();
     if (jj < S) {
       for (int xx = 0; xx < S; ++xx) {
-        float s = 0.0f, dp = 0.0f;
+        float sv = 0.0f, dp = 0.0f;
         for (int d = 0; d < D; ++d) {
-          s = fmaf(qt[xx * D + d], krow[d], s);
-          dp = fmaf(dot[xx * D + d], vrow[d], dp);
+          sv = fmaf(qt[xx * D + d], load_f(krow + d), sv);
+          dp = fmaf(dot[xx * D + d], load_f(vrow + d), dp);
         }
-        const float pw = wi * expf(s * attn_scale - lx[xx]);
+        const float pw = wi * expf(sv * attn_scale - lx[xx]);
         const float dsv = pw * (dp - dx[xx]);
-        for (int d = 0; d < D; ++d) {
-          dvrow[d] = fmaf(pw, dot[xx * D + d], dvrow[d]);
-          dkrow[d] = fmaf(attn_scale * dsv, qt[xx * D + d], dkrow[d]);
+#pragma unroll
+        for (int d = 0; d < 64; ++d) {
+          if (d < D) {
+            dva[d] = fmaf(pw, dot[xx * D + d], dva[d]);
+            dka[d] = fmaf(attn_scale * dsv, qt[xx * D + d], dka[d]);
+          }
+        }
+      }
+    }
+  }
+  if (jj < S) {
+    if (ACC) {
+#pragma unroll
+      for (int d = 0; d < 64; ++d) {
+        if (d < D) {
+          dka_out[d] = dka[d];
+          dva_out[d] = dva[d];
+        }
+      }
+    } else {
+      T* dkrow = (T*)dk + tile * tsz + (int64_t)jj * D;
+      T* dvrow = (T*)dv + tile * tsz + (int64_t)jj * D;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) {
+        if (d < D) {
+          store_f(dkrow + d, dka[d]);
+          store_f(dvrow + d, dva[d]);
         }
       }
     }
   }
   if (dlk) {
-    if (jj < dl) dlk[tile * dl + jj] = score_scale * dlk_acc[0];
-    if (jj + 64 < dl) dlk[tile * dl + jj + 64] = score_scale * dlk_acc[1];
+    if (jj < dl) put<ACC>(dlk + tile * dl + jj, score_scale * dlk_acc[0]);
+    if (jj + 64 < dl) put<ACC>(dlk + tile * dl + jj + 64, score_scale * dlk_acc[1]);
   }
+}
+
+template <typename T>
+static hipError_t launch_backward_gen(const LaunchBackward& a, int64_t qtiles, int64_t ktiles,
+                                      bool fork) {
+  hipError_t err;
+  if (qtiles > 0) {
+    KernelTimer timer(kKernBackwardQ, a.stream);
+    auto kern = a.accumulate ? k_bwd_q_gen<T, true> : k_bwd_q_gen<T, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)qtiles), dim3(64), 0, a.stream, (const T*)a.q,
+                       (const T*)a.kk, (const T*)a.v, a.idx, a.w, a.lse, (const T*)a.dout,
+                       (const T*)a.lk, (T*)a.dq, a.dw, a.dscore, a.dlq, a.delta, a.ds_layer,
+                       a.n_query, a.n_key, a.S, a.D, a.k, a.dl, a.attn_scale, a.score_scale);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
+  if (ktiles > 0) {
+    KernelTimer timer(kKernBackwardKV, a.stream);
+    auto kern = a.accumulate ? k_bwd_kv_gen<T, true> : k_bwd_kv_gen<T, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ktiles), dim3(64), 0, a.stream, (const T*)a.q,
+                       (const T*)a.kk, (const T*)a.v, a.w, a.lse, (const T*)a.dout, a.delta,
+                       a.rev_off, a.rev_ent, (const T*)a.lq, a.accumulate ? a.ds_layer : a.dscore,
+                       a.dk, a.dv, a.dlk, a.n_query, a.n_key, a.S, a.D, a.k, a.dl, a.attn_scale,
+                       a.score_scale);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_backward(const LaunchBackward& a) {
@@ -788,44 +895,34 @@ hipError_t launch_backward(const LaunchBackward& a) {
   if (err != hipSuccess) return err;
   if (fork && (err = hipEventRecord(a.join, a.side)) != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
-  if (a.dtype == 1) {
+  if (a.dtype == 1 && a.S == 64 && a.D == 64) {
     if (qtiles > 0) {
       KernelTimer timer(kKernBackwardQ, a.stream);
-      hipLaunchKernelGGL(k_bwd_q_bf16, dim3((unsigned)qtiles), dim3(256), 0, a.stream,
+      auto kern = a.accumulate ? k_bwd_q_bf16<true> : k_bwd_q_bf16<false>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)qtiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                          a.lse, (const bf16*)a.dout, (const bf16*)a.lk, (bf16*)a.dq, a.dw,
-                         a.dscore, a.dlq, a.delta, a.n_query, a.n_key, a.k, a.dl,
+                         a.dscore, a.dlq, a.delta, a.ds_layer, a.n_query, a.n_key, a.k, a.dl,
                          a.attn_scale, a.score_scale);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
-      hipLaunchKernelGGL(k_bwd_kv_bf16, dim3((unsigned)ktiles), dim3(256), 0, a.stream,
+      auto kern = a.accumulate ? k_bwd_kv_bf16<true> : k_bwd_kv_bf16<false>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)ktiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.w, a.lse,
                          (const bf16*)a.dout, a.delta, a.rev_off, a.rev_ent, (const bf16*)a.lq,
-                         a.dscore, (bf16*)a.dk, (bf16*)a.dv, a.dlk, a.n_query, a.n_key, a.k,
+                         a.accumulate ? a.ds_layer : a.dscore, a.dk, a.dv, a.dlk, a.n_query,
+                         a.n_key, a.k,
                          a.dl, a.attn_scale, a.score_scale);
     }
+  } else if (a.dtype == 1) {
+    err = launch_backward_gen<bf16>(a, qtiles, ktiles, fork);
+    if (err != hipSuccess) return err;
   } else {
-    if (qtiles > 0) {
-      KernelTimer timer(kKernBackwardQ, a.stream);
-      hipLaunchKernelGGL(k_bwd_q_f32, dim3((unsigned)qtiles), dim3(64), 0, a.stream,
-                         (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.idx, a.w,
-                         a.lse, (const float*)a.dout, (const float*)a.lk, (float*)a.dq, a.dw,
-                         a.dscore, a.dlq, a.delta, a.n_query, a.n_key, a.S, a.D, a.k, a.dl,
-                         a.attn_scale, a.score_scale);
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
-    if (ktiles > 0) {
-      KernelTimer timer(kKernBackwardKV, a.stream);
-      hipLaunchKernelGGL(k_bwd_kv_f32, dim3((unsigned)ktiles), dim3(64), 0, a.stream,
-                         (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.w, a.lse,
-                         (const float*)a.dout, a.delta, a.rev_off, a.rev_ent,
-                         (const float*)a.lq, a.dscore, (float*)a.dk, (float*)a.dv, a.dlk,
-                         a.n_query, a.n_key, a.S, a.D, a.k, a.dl, a.attn_scale, a.score_scale);
-    }
+    err = launch_backward_gen<float>(a, qtiles, ktiles, fork);
+    if (err != hipSuccess) return err;
   }
   return hipGetLastError();
 }

@@ -297,5 +297,8 @@ __device__ __forceinline__ bf16x8 lds_tr_operand16(const bf16* tile, int c_base,
 
 __device__ __forceinline__ float load_f(const float* p) { return *p; }
 __device__ __forceinline__ float load_f(const bf16* p) { return (float)(*p); }
+// One rounding of a float32 result to the element type (round to nearest even).
+__device__ __forceinline__ void store_f(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_f(bf16* p, float v) { *p = (bf16)v; }
 
 }  // namespace gca

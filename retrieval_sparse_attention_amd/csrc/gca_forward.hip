@@ -26,7 +26,8 @@
 //      no running rescale is needed.
 // O is rounded to bf16 once at the end.
 //
-// f32 path.  One thread per query row, float32 throughout (small workloads).
+// Generic path (other sizes, float32 or bf16 elements).  One thread per query
+// row, float32 arithmetic, one rounding of the output (small workloads).
 
 #include "gca_device.h"
 #include "gca_launch.h"
@@ -210,10 +211,13 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
   }
 }
 
-// float32 path: 64 threads per query chunk, thread x owns query row x (< S).
-__global__ __launch_bounds__(64) void k_fwd_f32(
-    const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
-    const int32_t* __restrict__ idx, const float* __restrict__ w, float* __restrict__ o,
+// Generic path (any S, D <= 64; float32 or bf16 elements): 64 threads per
+// query chunk, thread x owns query row x (< S); float32 arithmetic, with the
+// output row accumulated in registers and rounded to the element type once.
+template <typename T>
+__global__ __launch_bounds__(64) void k_fwd_gen(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ w, T* __restrict__ o,
     float* __restrict__ lse, int64_t n_query, int64_t n_key, int S, int D, int topk,
     float attn_scale) {
   __shared__ float kt[64 * 64];
@@ -223,10 +227,10 @@ __global__ __launch_bounds__(64) void k_fwd_f32(
   const int64_t tile = blockIdx.x;
   const int64_t head = tile / n_query;
   const int64_t tsz = (int64_t)S * D;
-  float* orow = o + tile * tsz + (int64_t)x * D;
-  const float* qrow = q + tile * tsz + (int64_t)x * D;
-  if (x < S)
-    for (int d = 0; d < D; ++d) orow[d] = 0.0f;
+  const T* qrow = q + tile * tsz + (int64_t)x * D;
+  float oa[64];
+#pragma unroll
+  for (int d = 0; d < 64; ++d) oa[d] = 0.0f;
   for (int i = 0; i < topk; ++i) {
     const int c = idx[tile * topk + i];
     const float wi = w[tile * topk + i];
@@ -236,11 +240,11 @@ __global__ __launch_bounds__(64) void k_fwd_f32(
       continue;
     }
     __syncthreads();
-    const float* ks = kk + (head * n_key + c) * tsz;
-    const float* vs = v + (head * n_key + c) * tsz;
+    const T* ks = kk + (head * n_key + c) * tsz;
+    const T* vs = v + (head * n_key + c) * tsz;
     for (int e = x; e < S * D; e += 64) {
-      kt[e] = ks[e];
-      vt[e] = vs[e];
+      kt[e] = load_f(ks + e);
+      vt[e] = load_f(vs + e);
     }
     __syncthreads();
     if (x < S) {
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(
       float m = -__builtin_huge_valf();
       for (int j = 0; j < S; ++j) {
         float acc = 0.0f;
-        for (int d = 0; d < D; ++d) acc = fmaf(qrow[d], kt[j * D + d], acc);
+        for (int d = 0; d < D; ++d) acc = fmaf(load_f(qrow + d), kt[j * D + d], acc);
         p[j] = acc * attn_scale;
         m = fmaxf(m, p[j]);
       }
@@ -259,12 +263,21 @@ __global__ __launch_bounds__(64) void k_fwd_f32(
       }
       if (lse_row) lse_row[x] = m + logf(l);
       const float sc = wi / l;
-      for (int d = 0; d < D; ++d) {
-        float acc = 0.0f;
-        for (int j = 0; j < S; ++j) acc = fmaf(p[j], vt[j * D + d], acc);
-        orow[d] += sc * acc;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) {
+        if (d < D) {
+          float acc = 0.0f;
+          for (int j = 0; j < S; ++j) acc = fmaf(p[j], vt[j * D + d], acc);
+          oa[d] = fmaf(sc, acc, oa[d]);
+        }
       }
     }
+  }
+  if (x < S) {
+    T* orow = o + tile * tsz + (int64_t)x * D;
+#pragma unroll
+    for (int d = 0; d < 64; ++d)
+      if (d < D) store_f(orow + d, oa[d]);
   }
 }
 
@@ -272,12 +285,16 @@ hipError_t launch_forward(const LaunchForward& a) {
   const int64_t tiles = a.G * a.B * a.H * a.n_query;
   if (tiles == 0) return hipSuccess;
   KernelTimer timer(kKernForward, a.stream);
-  if (a.dtype == 1) {
+  if (a.dtype == 1 && a.S == 64 && a.D == 64) {
     hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(256), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                        (bf16*)a.o, a.lse, a.n_query, a.n_key, a.k, a.attn_scale);
+  } else if (a.dtype == 1) {
+    hipLaunchKernelGGL(k_fwd_gen<bf16>, dim3((unsigned)tiles), dim3(64), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
+                       (bf16*)a.o, a.lse, a.n_query, a.n_key, a.S, a.D, a.k, a.attn_scale);
   } else {
-    hipLaunchKernelGGL(k_fwd_f32, dim3((unsigned)tiles), dim3(64), 0, a.stream,
+    hipLaunchKernelGGL(k_fwd_gen<float>, dim3((unsigned)tiles), dim3(64), 0, a.stream,
                        (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.idx, a.w,
                        (float*)a.o, a.lse, a.n_query, a.n_key, a.S, a.D, a.k, a.attn_scale);
   }

@@ -66,7 +66,9 @@ struct LaunchBackward {
   float* dscore;
   float* dlq;
   float* dlk;
+  int accumulate;    // 1: dk, dv (float32), dw, dscore, dlq, dlk are accumulators added to
   float* delta;      // workspace [heads * n_query * k * S]: rowsum(P * dP) per pair
+  float* ds_layer;   // workspace [heads * n_query * k]: this call's dscore (accumulate mode)
   int32_t* rev_off;  // workspace [heads * (n_key + 1)]
   int32_t* rev_ent;  // workspace [heads * n_query * k]: q * k + slot, grouped by chunk
   hipStream_t stream;

@@ -48,8 +48,10 @@ def _status(fn, *args):
 def test_workspace_sizes():
     s = _bf16_shape()
     assert gca.gca_workspace_size(s, gca.OP_FORWARD) == 0
-    # delta: 96 heads * 256 * 8 * 64 floats; rev_off: 96 * 257 ints; rev_ent: 96 * 2048 ints
-    expect = 96 * 256 * 8 * 64 * 4 + ((96 * 257 * 4 + 255) // 256) * 256 + 96 * 2048 * 4
+    # delta: 96 heads * 256 * 8 * 64 floats; rev_off: 96 * 257 ints; rev_ent: 96 * 2048 ints;
+    # one layer's dscore (accumulate mode): 96 * 2048 floats
+    expect = (96 * 256 * 8 * 64 * 4 + ((96 * 257 * 4 + 255) // 256) * 256 + 96 * 2048 * 4
+              + 96 * 2048 * 4)
     assert gca.gca_workspace_size(s, gca.OP_BACKWARD) == expect
     assert gca.gca_workspace_size(s, gca.OP_RETRIEVE) == 0  # 256 candidates: one slice
     big = _bf16_shape(G=1, B=1, n_query=32, n_key=262144, softmax_one=0)
@@ -58,7 +60,7 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("over,code", [
     (dict(G=0), 1), (dict(n_key=-1), 1), (dict(top_k=0), 1), (dict(top_k=17), 2),
-    (dict(dtype=7), 1), (dict(softmax_one=2), 1), (dict(chunk_size=32), 2),
+    (dict(dtype=7), 1), (dict(softmax_one=2), 1), (dict(chunk_size=65), 2),
     (dict(head_dim=128), 2), (dict(landmark_dim=48), 2), (dict(n_key=2 ** 31), 1),
     (dict(attn_scale=float("inf")), 1),
 ])
@@ -67,6 +69,24 @@ def test_bad_shapes(over, code):
     n = ctypes.c_size_t(0)
     st, msg = _status("gca_workspace_size", ctypes.byref(s), 2, ctypes.byref(n))
     assert st == code and msg
+
+
+def test_bf16_attention_sizes():
+    # S in {16, 64} x D in {32, 64} and other sizes up to 64 are accepted;
+    # beyond 64 they are not
+    for S, D in ((16, 32), (16, 64), (64, 32), (64, 64), (5, 7)):
+        s = _bf16_shape(chunk_size=S, head_dim=D)
+        assert gca.gca_workspace_size(s, gca.OP_BACKWARD) > 0
+        assert gca.gca_workspace_size(s, gca.OP_FORWARD) == 0
+    n = ctypes.c_size_t(0)
+    for S, D in ((128, 64), (64, 96)):
+        bad = _bf16_shape(chunk_size=S, head_dim=D)
+        st, msg = _status("gca_workspace_size", ctypes.byref(bad), 1, ctypes.byref(n))
+        assert st == 2 and "<= 64" in msg
+    # the non-negative scale condition holds only for the 64 x 64 MFMA forward
+    s = _bf16_shape(chunk_size=16, head_dim=32, attn_scale=-0.5)
+    st, msg = _status("gca_forward", ctypes.byref(s), None, A, A, A, A, A, None, None)
+    assert st == 1 and "q is NULL" in msg
 
 
 def test_f32_limits():
@@ -154,7 +174,7 @@ def test_gather_rejects_before_any_device_call():
     assert st == 1 and "k_packed" in msg and "aligned" in msg
     st, msg = _status("gca_gather_kv", ctypes.byref(s), A, None, A, A, A, A, None)
     assert st == 1 and "k is NULL" in msg
-    bad = _bf16_shape(chunk_size=32)
+    bad = _bf16_shape(chunk_size=80)
     assert _status("gca_gather_kv", ctypes.byref(bad), A, A, A, A, A, A, None)[0] == 2
     empty = _bf16_shape(n_query=0)
     assert _status("gca_gather_kv", ctypes.byref(empty), None, None, None, None, None, None,

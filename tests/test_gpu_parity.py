@@ -78,6 +78,13 @@ def test_bf16_top_k_sizes(k):
     _full_path("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=48, n_key=48, k=k)
 
 
+@pytest.mark.parametrize("S,D", [(16, 32), (16, 64), (64, 32), (5, 7)])
+def test_bf16_chunk_and_head_sizes(S, D):
+    # bf16 attention beyond 64 x 64 tiles (the float32 VALU path): every output
+    # of retrieve -> forward -> backward against the oracle, two groups
+    _full_path("train16k_fwdbwd_g2", B=1, H=2, n_query=40, n_key=40, S=S, D=D)
+
+
 def test_bf16_landmark_dim_32():
     _full_path("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=40, n_key=40, Dl=32)
 
