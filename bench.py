@@ -35,8 +35,6 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-heads", type=int, default=96,
-                    help="(g, b, h) heads of one step the oracle runs for the CPU baseline")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the 16M-token retrieval and 1M-token inference measurements")
     ap.add_argument("--infer-steps", type=int, default=1000)
@@ -137,32 +135,160 @@ def traffic_for(kernel, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, cfg, n_heads):
-    """The float64 oracle on `n_heads` (g, b, h) heads of one step, one thread."""
-    from threadpoolctl import threadpool_limits
+# --------------------------------------------------------------------------
+# CPU baseline: the float64 oracle, timed on the host cores beside the GPU run.
+# Its inputs are generated before anything touches the GPU and a pool of
+# worker processes is forked then, so the workers share the inputs and never
+# inherit GPU state.  Each worker runs the oracle with BLAS on one thread.
+# --------------------------------------------------------------------------
+_CPU = {}  # inputs the oracle workers read (filled before the pool is forked)
 
+
+def cpu_workers():
+    """Oracle worker processes: the cores this process may use, at most 16
+    (OMP_NUM_THREADS when set, e.g. a one-GPU share of a larger host)."""
+    n = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    return max(1, min(n, cap, 16))
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    global _BLAS_LIMIT
+    _BLAS_LIMIT = threadpool_limits(1)
+
+
+class _HostTiles:
+    """K or V of one head at a long context, for the oracle: chunk c's tile is
+    pool[(salt + 7919 c) mod len(pool)], a pool of host-drawn N(0,1)/8 tiles
+    rounded to bf16 (the device-drawn K/V are never copied back).  The oracle
+    only indexes it by chunk and reads its length."""
+
+    def __init__(self, pool, n_key, salt):
+        self.pool, self.salt = pool, salt
+        self.shape = (n_key,) + tuple(pool.shape[1:])
+
+    def __getitem__(self, c):
+        return self.pool[(self.salt + 7919 * int(c)) % self.pool.shape[0]]
+
+
+def _tile_pool(S, D, seed, n=512):
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed)
+    t = torch.from_numpy((rng.standard_normal((n, S, D)) / 8).astype(np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _cpu_job(job):
+    """One oracle job in a worker; returns the number of units it did."""
     from oracle import gca_oracle as orc
-    G, B, H = cfg["G"], cfg["B"], cfg["H"]
-    heads = [(g, b, h) for g in range(G) for b in range(B) for h in range(H)][:n_heads]
+    kind, arg = job
     f = lambda t: t.to("cpu").double().numpy()
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for (g, b, h) in heads:
+    if kind in ("train", "fwd"):
+        d = _CPU[kind]
+        x, cfg = d["x"], d["cfg"]
+        for (g, b, h) in arg:
             sl = lambda t: f(t[g:g + 1, b:b + 1, h:h + 1])
-            q, k, v, do = sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["dout"])
-            lq, lk = sl(x["lq"]), sl(x["lk"])
+            q, k, v, lq, lk = sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["lq"]), sl(x["lk"])
             idx, _, w = orc.retrieve(lq, lk, x["q_pos"].numpy(), cfg["k"], cfg["score_scale"],
                                      cfg["softmax_one"])
             orc.forward(q, k, v, idx, w, cfg["attn_scale"])
-            orc.backward(q, k, v, idx, w, do, lq, lk, cfg["attn_scale"], cfg["score_scale"])
-        dt = time.perf_counter() - t0
-    total_heads = G * B * H
-    step_s = dt * total_heads / len(heads)
-    tokens = cfg["B"] * cfg["n_query"] * cfg["S"]
-    return dict(value=round(tokens / step_s, 2), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{len(heads)} of {total_heads} (g,b,h) heads of one step "
-                       f"(retrieve+forward+backward, float64 numpy, BLAS limited to 1 thread), "
-                       f"{dt:.1f} s, scaled by {total_heads}/{len(heads)}")
+            if kind == "train":
+                orc.backward(q, k, v, idx, w, sl(x["dout"]), lq, lk, cfg["attn_scale"],
+                             cfg["score_scale"])
+        return len(arg)
+    if kind == "infer1m":
+        d = _CPU[kind]
+        cfg, lk = d["cfg"], d["lk"]
+        H = cfg["H"]
+        lk64 = [f(lk[0, 0, h]) for h in range(H)]
+        kt = [_HostTiles(d["kpool"], cfg["n_key"], 11 * h) for h in range(H)]
+        vt = [_HostTiles(d["vpool"], cfg["n_key"], 13 * h + 5) for h in range(H)]
+        q_pos = int(d["q_pos"])
+        for s in arg:
+            for h in range(H):
+                lq_row = f(d["lqs"][s, 0, 0, h, 0])
+                idx, _, w = orc.retrieve_one(lq_row, lk64[h], q_pos, cfg["k"],
+                                             cfg["score_scale"], cfg["softmax_one"])
+                orc.forward_query_chunk(f(d["qs"][s, 0, 0, h, 0]), kt[h], vt[h], idx, w,
+                                        cfg["attn_scale"])
+        return len(arg)
+    if kind == "retrieve16m":
+        d = _CPU[kind]
+        cfg, h = d["cfg"], arg
+        lk64 = f(d["lk"][0, 0, h])
+        kt = _HostTiles(d["kpool"], cfg["n_key"], 11 * h)
+        vt = _HostTiles(d["vpool"], cfg["n_key"], 13 * h + 5)
+        q_pos = int(d["q_pos"][0])
+        for n in range(cfg["n_query"]):
+            idx, _, w = orc.retrieve_one(f(d["lq"][0, 0, h, n]), lk64, q_pos, cfg["k"],
+                                         cfg["score_scale"], cfg["softmax_one"])
+            orc.forward_query_chunk(f(d["q"][0, 0, h, n]), kt, vt, idx, w, cfg["attn_scale"])
+        return cfg["n_query"]
+    raise ValueError(kind)
+
+
+def _run_jobs(pool, jobs):
+    t0 = time.perf_counter()
+    units = sum(pool.map(_cpu_job, jobs, chunksize=1))
+    return time.perf_counter() - t0, units
+
+
+def _split(items, n):
+    n = max(1, min(n, len(items)))
+    return [items[i::n] for i in range(n)]
+
+
+def cpu_baselines(pool, workers):
+    """The oracle on each measured workload, all workers; one dict per workload."""
+    out = {}
+    blas = "BLAS limited to 1 thread per worker process"
+    if "train" in _CPU:
+        cfg = _CPU["train"]["cfg"]
+        heads = [(g, b, h) for g in range(cfg["G"]) for b in range(cfg["B"])
+                 for h in range(cfg["H"])]
+        parts = _split(heads, workers)
+        dt, n = _run_jobs(pool, [("train", p) for p in parts])
+        tokens = cfg["B"] * cfg["n_query"] * cfg["S"]
+        out["train"] = dict(value=round(tokens / dt, 2), unit="tokens/s", cores=len(parts),
+                            kind="oracle", blas_threads=1,
+                            sample=f"the whole step: all {n} (g,b,h) heads, retrieve + forward + "
+                                   f"backward, float64 numpy, {len(parts)} worker processes, "
+                                   f"{blas}; {dt:.2f} s wall")
+    if "fwd" in _CPU:
+        cfg = _CPU["fwd"]["cfg"]
+        heads = [(g, b, h) for g in range(cfg["G"]) for b in range(cfg["B"])
+                 for h in range(cfg["H"])]
+        parts = _split(heads, workers)
+        dt, n = _run_jobs(pool, [("fwd", p) for p in parts])
+        tokens = cfg["B"] * cfg["n_query"] * cfg["S"]
+        out["fwd"] = dict(value=round(tokens / dt, 2), unit="tokens/s", cores=len(parts),
+                          kind="oracle", blas_threads=1,
+                          sample=f"all {n} (g,b,h) heads, retrieve + forward, float64 numpy, "
+                                 f"{len(parts)} worker processes, {blas}; {dt:.2f} s wall")
+    if "infer1m" in _CPU:
+        steps = list(range(_CPU["infer1m"]["lqs"].shape[0]))
+        parts = _split(steps, workers)
+        dt, n = _run_jobs(pool, [("infer1m", p) for p in parts])
+        out["infer1m"] = dict(value=round(n / dt, 2), unit="steps/s", cores=len(parts),
+                              kind="oracle", blas_threads=1,
+                              us_per_step_amortised=round(dt / n * 1e6, 1),
+                              sample=f"all {n} chunk steps x 12 heads (scan of 16383 landmarks, "
+                                     f"top-8, 8-chunk attention), steps split over "
+                                     f"{len(parts)} worker processes, {blas}; K/V tiles drawn "
+                                     f"on the host (same distribution); {dt:.2f} s wall")
+    if "retrieve16m" in _CPU:
+        H = _CPU["retrieve16m"]["cfg"]["H"]
+        jobs = [("retrieve16m", h) for h in range(H)]
+        dt, n = _run_jobs(pool, jobs)
+        out["retrieve16m"] = dict(value=round(dt * 1e3, 2), unit="ms (retrieve + forward)",
+                                  cores=min(workers, H), kind="oracle", blas_threads=1,
+                                  sample=f"the whole batch: {n} query chunks x 262144 resident "
+                                         f"chunks, one worker process per head ({H} heads on "
+                                         f"{min(workers, H)} workers), {blas}; K/V tiles drawn "
+                                         f"on the host (same distribution); {dt:.2f} s wall")
+    return out
 
 
 def _timed(fn, reps):
@@ -260,7 +386,7 @@ def bench_swa(steps):
                     "pair instead of 5); flops above count the 5 the math needs"}
 
 
-def bench_train16k_fwd(steps):
+def bench_train16k_fwd(steps, x=None):
     """The 16K-token forward of one group (G=1, vanilla weights, aliased landmarks):
     gca_retrieve + gca_forward per step, against max(HBM, MFMA) time of the forward's
     algorithmic bytes and flops."""
@@ -270,7 +396,8 @@ def bench_train16k_fwd(steps):
     import synth
     name = "train16k_fwd"
     cfg = synth.workload(name)
-    x = synth.training_inputs(name, with_dout=False)
+    if x is None:
+        x = synth.training_inputs(name, with_dout=False)
     d = {key: val.contiguous().cuda() for key, val in x.items() if key != "cfg"}
     G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
     S, D, Dl, k = cfg["S"], cfg["D"], cfg["Dl"], cfg["k"]
@@ -335,7 +462,18 @@ def bench_cold_and_copy(step, reps=5):
             "copy_1GiB_read_plus_write_GBps": round(2 * 2**30 / copy_s / 1e9, 1)}
 
 
-def bench_retrieve16m(reps=20):
+def long_context_inputs(name, steps=1):
+    """Resident landmarks and the query chunk batches (one per step) of a
+    long-context workload, on the host."""
+    import torch
+
+    import synth
+    lk = synth.context_landmarks(name)
+    lk64 = lk.to(torch.float64).numpy()
+    return lk, [synth.query_batch(name, lk, step=s, lk64=lk64) for s in range(steps)]
+
+
+def bench_retrieve16m(reps=20, inp=None):
     """16,777,216-token resident context (262144 chunks of 64, K/V ~51.5 GB):
     32 query chunks retrieve top-8 from every chunk, then attend and fuse."""
     import torch
@@ -344,8 +482,7 @@ def bench_retrieve16m(reps=20):
     import synth
     name = "retrieve16m"
     cfg = synth.workload(name)
-    lk = synth.context_landmarks(name)
-    qb = synth.query_batch(name, lk)
+    lk, (qb,) = inp if inp is not None else long_context_inputs(name)
     kd, vd = synth.device_kv(name, "cuda")
     lkd, lqd, qd = lk.cuda(), qb["lq"].cuda(), qb["q"].cuda()
     qpos = qb["q_pos"].cuda()
@@ -389,7 +526,7 @@ def bench_retrieve16m(reps=20):
             "needle_hit_rate": hits, "reps": reps}
 
 
-def bench_infer1m(steps):
+def bench_infer1m(steps, inp=None):
     """1,048,576-token resident context (16384 chunks): per chunk step, one new
     query chunk retrieves top-8 of 16383 candidates (with a planted needle),
     attends and fuses.  Latency of each step from HIP events."""
@@ -400,12 +537,10 @@ def bench_infer1m(steps):
     import synth
     name = "infer1m_step"
     cfg = synth.workload(name)
-    lk = synth.context_landmarks(name)
+    lk, batches = inp if inp is not None else long_context_inputs(name, steps)
     kd, vd = synth.device_kv(name, "cuda")
     lkd = lk.cuda()
     G, B, H, Nk, S, k = cfg["G"], cfg["B"], cfg["H"], cfg["n_key"], cfg["S"], cfg["k"]
-    lk64 = lk.to(torch.float64).numpy()
-    batches = [synth.query_batch(name, lk, step=s, lk64=lk64) for s in range(steps)]
     qs = torch.stack([b["q"] for b in batches]).cuda()
     lqs = torch.stack([b["lq"] for b in batches]).cuda()
     needles = torch.stack([b["needle"] for b in batches])
@@ -505,7 +640,7 @@ def bench_infer1m_graph(shape, lqs, qs, lkd, kd, vd, qpos, ws, idx_eager, o_eage
             "replays_equal_eager_bits": bool(exact)}
 
 
-def bench_infer1m_offload(steps):
+def bench_infer1m_offload(steps, inp=None):
     """The 1M-token inference step with K/V offloaded to pinned host memory:
     landmarks stay in HBM; per step the scan picks 8 chunks per head, only
     those tiles cross the host link (gca_gather_kv), and the forward runs on
@@ -518,7 +653,6 @@ def bench_infer1m_offload(steps):
     import synth
     name = "infer1m_step"
     cfg = synth.workload(name)
-    lk = synth.context_landmarks(name)
     kd, vd = synth.device_kv(name, "cuda")
     kh = torch.empty(tuple(kd.shape), dtype=kd.dtype, pin_memory=True)
     vh = torch.empty(tuple(vd.shape), dtype=vd.dtype, pin_memory=True)
@@ -531,10 +665,12 @@ def bench_infer1m_offload(steps):
     offload_s = time.perf_counter() - t0
     del kd, vd
     torch.cuda.empty_cache()
+    if inp is not None:
+        lk, batches = inp
+    else:
+        lk, batches = long_context_inputs(name, steps)
     lkd = lk.cuda()
     G, B, H, Nk, S, k = cfg["G"], cfg["B"], cfg["H"], cfg["n_key"], cfg["S"], cfg["k"]
-    lk64 = lk.to(torch.float64).numpy()
-    batches = [synth.query_batch(name, lk, step=s, lk64=lk64) for s in range(steps)]
     qs = torch.stack([b["q"] for b in batches]).cuda()
     lqs = torch.stack([b["lq"] for b in batches]).cuda()
     needles = torch.stack([b["needle"] for b in batches])
@@ -605,12 +741,39 @@ def main():
     import retrieval_sparse_attention_amd as gca
     import synth
 
+    # Host inputs of every leg first, then the oracle's worker pool, forked
+    # before anything touches the GPU (the workers inherit the inputs).
+    cfg = synth.workload(WORKLOAD)
+    x = synth.training_inputs(WORKLOAD)
+    x_fwd = None if args.no_extras else synth.training_inputs("train16k_fwd", with_dout=False)
+    inp16m = inp1m = None
+    if not args.no_long_context:
+        inp16m = long_context_inputs("retrieve16m")
+        inp1m = long_context_inputs("infer1m_step", args.infer_steps)
+    pool, workers = None, 0
+    if not args.no_cpu_baseline:
+        import multiprocessing as mp
+        _CPU["train"] = dict(x=x, cfg=cfg)
+        if x_fwd is not None:
+            _CPU["fwd"] = dict(x=x_fwd, cfg=synth.workload("train16k_fwd"))
+        if inp1m is not None:
+            c1 = synth.workload("infer1m_step")
+            lk1, batches = inp1m
+            _CPU["infer1m"] = dict(cfg=c1, lk=lk1, q_pos=c1["q_pos"],
+                                   lqs=torch.stack([b["lq"] for b in batches]),
+                                   qs=torch.stack([b["q"] for b in batches]),
+                                   kpool=_tile_pool(64, 64, 41), vpool=_tile_pool(64, 64, 42))
+        if inp16m is not None:
+            lk16, (qb16,) = inp16m
+            _CPU["retrieve16m"] = dict(cfg=synth.workload("retrieve16m"), lk=lk16,
+                                       lq=qb16["lq"], q=qb16["q"], q_pos=qb16["q_pos"],
+                                       kpool=_tile_pool(64, 64, 51), vpool=_tile_pool(64, 64, 52))
+        workers = cpu_workers()
+        pool = mp.get_context("fork").Pool(workers, initializer=_worker_init)
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a ROCm GPU")
     gca.load()
     torch.cuda.set_device(0)
-    cfg = synth.workload(WORKLOAD)
-    x = synth.training_inputs(WORKLOAD)
     d = {key: val.contiguous().cuda() for key, val in x.items() if key != "cfg"}
     G, B, H, Nq, Nk = cfg["G"], cfg["B"], cfg["H"], cfg["n_query"], cfg["n_key"]
     S, D, Dl, k = cfg["S"], cfg["D"], cfg["Dl"], cfg["k"]
@@ -720,7 +883,7 @@ def main():
         extra = bench_cold_and_copy(step)
         print(f"[bench] cold step: {extra['cold_ms_per_step_median']} ms", file=sys.stderr,
               flush=True)
-        fwd16k = bench_train16k_fwd(args.steps)
+        fwd16k = bench_train16k_fwd(args.steps, x_fwd)
         print(f"[bench] 16K forward (one group): {fwd16k['ms_per_step']} ms", file=sys.stderr,
               flush=True)
     gumbel = None
@@ -732,19 +895,30 @@ def main():
               file=sys.stderr, flush=True)
     long_ctx = {}
     if not args.no_long_context:
-        long_ctx["retrieve16m"] = bench_retrieve16m()
+        long_ctx["retrieve16m"] = bench_retrieve16m(inp=inp16m)
         print(f"[bench] 16M retrieval: {long_ctx['retrieve16m']['retrieve_fwd_latency_ms']} ms",
               file=sys.stderr, flush=True)
-        long_ctx["infer1m_step"] = bench_infer1m(args.infer_steps)
+        long_ctx["infer1m_step"] = bench_infer1m(args.infer_steps, inp1m)
         print(f"[bench] 1M inference step p50: "
               f"{long_ctx['infer1m_step']['step_latency_us_p50']} us", file=sys.stderr, flush=True)
-        long_ctx["infer1m_step_offloaded_kv"] = bench_infer1m_offload(args.infer_steps)
+        long_ctx["infer1m_step_offloaded_kv"] = bench_infer1m_offload(args.infer_steps, inp1m)
         print(f"[bench] 1M inference step, K/V in host memory, p50: "
               f"{long_ctx['infer1m_step_offloaded_kv']['step_latency_us_p50']} us",
               file=sys.stderr, flush=True)
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, cfg, args.cpu_heads)
+    if pool is not None:
+        print(f"[bench] CPU baseline: the oracle on {workers} worker processes",
+              file=sys.stderr, flush=True)
+        base = cpu_baselines(pool, workers)
+        pool.close()
+        pool.join()
+        cpu = base.get("train")
+        if fwd16k is not None and "fwd" in base:
+            fwd16k["cpu_baseline"] = base["fwd"]
+        if "infer1m" in base:
+            long_ctx["infer1m_step"]["cpu_baseline"] = base["infer1m"]
+        if "retrieve16m" in base:
+            long_ctx["retrieve16m"]["cpu_baseline"] = base["retrieve16m"]
     line = {
         "metric": "GCA fwd+bwd tokens/s @16K ctx k=8",
         "value": round(value, 1),
