@@ -633,6 +633,17 @@ static gca_status backward_impl(const char* fn, int accumulate, const gca_shape*
   a.rev_ent = (int32_t*)((char*)ws + wl.rev_ent);
   a.ds_layer = (float*)((char*)ws + wl.ds_layer);
   a.stream = (hipStream_t)stream;
+  // A call on a stream under graph capture runs everything on that stream:
+  // forking onto the shared side stream would put the side stream into the
+  // capture, and an eager call from another thread meanwhile would then
+  // enqueue into someone else's graph.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(a.stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    capture = hipStreamCaptureStatusActive;  // unknown: take the single-stream path
+  }
+  if (capture != hipStreamCaptureStatusNone)
+    return device_status(gca::launch_backward(a), a.stream, fn);
   std::lock_guard<std::mutex> lock(g_side_mu);
   if (SideResources* sr = side_resources()) {
     a.side = sr->stream;

@@ -4,6 +4,8 @@ forward + backward) can be captured and replayed.  Every replay, with eager
 work and synchronisations between replays, must reproduce the eager step's
 outputs bit for bit (same kernels, same fixed summation order)."""
 
+import threading
+
 import pytest
 import torch
 
@@ -72,3 +74,77 @@ def test_training_step_replays_match_eager():
         torch.cuda.synchronize()
         for key, val in out.items():
             assert torch.equal(val, eager[key]), (r, key)
+
+
+def test_eager_backward_in_another_thread_during_a_capture():
+    """A backward being captured on one thread and an eager backward on another
+    thread's stream at the same time: the captured call runs on its own stream
+    only, so the eager call's fork onto the library's side stream is untouched
+    by the capture.  Replays and the eager call reproduce the reference bits."""
+    name, over = "train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72)
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    G, B, H, Nq, k = shape.G, shape.B, shape.H, shape.n_query, shape.top_k
+    idx = torch.empty((G, B, H, Nq, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((G, B, H, Nq, k), device="cuda")
+    w = torch.empty_like(score)
+    lse = torch.empty((G, B, H, Nq, k, 64), device="cuda")
+    o = torch.empty_like(d["q"])
+    gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], idx, score, w)
+    gca.gca_forward(shape, d["q"], d["k"], d["v"], idx, w, o, lse)
+    torch.cuda.synchronize()
+
+    def buffers():
+        return dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]),
+                    dv=torch.empty_like(d["v"]), dw=torch.empty_like(w),
+                    dscore=torch.empty_like(w), dlq=torch.empty(tuple(d["lq"].shape), device="cuda"),
+                    dlk=torch.empty(tuple(d["lk"].shape), device="cuda"),
+                    ws=torch.empty(gca.gca_workspace_size(shape, gca.OP_BACKWARD),
+                                   dtype=torch.uint8, device="cuda"))
+
+    def backward(b):
+        gca.gca_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"],
+                         b["dq"], b["dk"], b["dv"], b["dw"], b["dscore"], b["dlq"], b["dlk"],
+                         ws=b["ws"])
+
+    ref = buffers()
+    backward(ref)
+    torch.cuda.synchronize()
+    cap, eager = buffers(), buffers()
+    eager_stream = torch.cuda.Stream()
+    errors = []
+
+    def eager_call():
+        try:
+            with torch.cuda.stream(eager_stream):
+                backward(eager)
+            eager_stream.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        backward(cap)  # warm-up of the capture's buffers, as torch recommends
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        backward(cap)
+        t = threading.Thread(target=eager_call)
+        t.start()
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+        assert torch.equal(eager[key], ref[key]), ("eager", key)
+    for r in range(3):
+        for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+            cap[key].fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+            assert torch.equal(cap[key], ref[key]), (r, key)
