@@ -337,13 +337,9 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
  *   ws / ws_bytes  workspace (gca_workspace_size op 2)
  * dlq needs lk (unless n_key = 0); dlk needs lq.
  *
- * Streams: the call forks a second stream of the library (per device) off
- * `stream` for the reverse index of the retrieved chunks, which runs beside
- * the query-side kernel, and joins it back before the key-side kernel; to the
- * caller the work is ordered on `stream` as usual.  While `stream` is being
- * captured into a HIP graph the call does not fork: everything is enqueued on
- * `stream` alone, so the shared second stream never joins a capture and
- * eager calls from other threads meanwhile are unaffected.
+ * Streams: three kernels (the reverse index of the retrieved chunks, the
+ * query side, the key side) run in order on `stream`; the call keeps no
+ * stream or event of its own, so it can be captured into a HIP graph.
  */
 gca_status gca_backward(const gca_shape* shape, const void* q, const void* k,
                         const void* v, const int32_t* idx, const float* w,

@@ -7,7 +7,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 
 #include "gca.h"
 #include "gca_launch.h"
@@ -202,41 +201,6 @@ gca_status readable_on_device(const void* p, const char* name, const void** dev)
     *dev = p;
   }
   return GCA_OK;
-}
-
-// Per-device side stream and fork/join events of gca_backward, created on
-// first use (default priority, non-blocking) and kept until the process ends.
-// The mutex covers the whole enqueue of a backward call, so that concurrent
-// callers never interleave records of the shared events.
-struct SideResources {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool ready = false, failed = false;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideResources g_side[kMaxDevices];
-
-// The calling thread's device's resources, or nullptr (then the backward
-// runs on the caller's stream alone).  Call with g_side_mu held.
-SideResources* side_resources() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  SideResources& r = g_side[dev];
-  if (!r.ready && !r.failed) {
-    if (hipStreamCreateWithFlags(&r.stream, hipStreamNonBlocking) == hipSuccess &&
-        hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) == hipSuccess &&
-        hipEventCreateWithFlags(&r.join, hipEventDisableTiming) == hipSuccess) {
-      r.ready = true;
-    } else {
-      (void)hipGetLastError();
-      r.failed = true;
-    }
-  }
-  return r.ready ? &r : nullptr;
 }
 
 #define GCA_TRY(expr)                 \
@@ -633,23 +597,6 @@ static gca_status backward_impl(const char* fn, int accumulate, const gca_shape*
   a.rev_ent = (int32_t*)((char*)ws + wl.rev_ent);
   a.ds_layer = (float*)((char*)ws + wl.ds_layer);
   a.stream = (hipStream_t)stream;
-  // A call on a stream under graph capture runs everything on that stream:
-  // forking onto the shared side stream would put the side stream into the
-  // capture, and an eager call from another thread meanwhile would then
-  // enqueue into someone else's graph.
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(a.stream, &capture) != hipSuccess) {
-    (void)hipGetLastError();
-    capture = hipStreamCaptureStatusActive;  // unknown: take the single-stream path
-  }
-  if (capture != hipStreamCaptureStatusNone)
-    return device_status(gca::launch_backward(a), a.stream, fn);
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  if (SideResources* sr = side_resources()) {
-    a.side = sr->stream;
-    a.fork = sr->fork;
-    a.join = sr->join;
-  }
   return device_status(gca::launch_backward(a), a.stream, fn);
 }
 

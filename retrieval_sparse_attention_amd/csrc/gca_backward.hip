@@ -36,22 +36,30 @@ namespace gca {
 //   1. the entries are cut into 8 segments, one per wave; per pass over 512
 //      key chunks each wave counts the chunks of its segment (LDS atomics);
 //   2. an exclusive scan over (chunk, segment) gives every segment its own
-//      write cursor per chunk;
-//   3. each wave places its entries 64 at a time: a lane's rank among the
-//      earlier lanes with the same chunk comes from a compare loop over the
-//      64 chunk ids in LDS, so all lanes write in parallel and the order
-//      inside each list is the entry order.
+//      write cursor per chunk (a wave scan of the chunk totals, then the
+//      8 wave sums through LDS);
+//   3. each wave places its entries 64 at a time.  A lane's rank among the
+//      earlier lanes with the same chunk comes from ten ballots, one per bit
+//      of the chunk number within the pass (and one for "not in this pass"):
+//      AND-ing each ballot or its complement, as the lane's own bit says,
+//      leaves exactly the lanes whose chunk equals the lane's, and the
+//      population count of that mask below the lane is the rank.  All lanes
+//      write in parallel and the order inside each list is the entry order.
+// RES: every segment has at most 512 entries, which stay in registers
+// between the counting and the placing sweep (one read of idx).
 // ---------------------------------------------------------------------------
 constexpr int kRevWaves = 8;
 constexpr int kRevKeys = 512;  // key chunks per pass = threads per workgroup
+constexpr int kRevKeyBits = 10;  // bits of a chunk within a pass, plus "outside the pass"
 
+template <bool RES>
 __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict__ idx,
                                                        int64_t n_query, int64_t n_key, int topk,
                                                        int32_t* __restrict__ rev_off,
                                                        int32_t* __restrict__ rev_ent) {
+  static_assert((1 << (kRevKeyBits - 1)) == kRevKeys, "one bit above the chunk bits");
   __shared__ int cnt[kRevWaves][kRevKeys];
-  __shared__ int part[kRevKeys];
-  __shared__ __align__(16) int kbuf[kRevWaves][64];
+  __shared__ int wsum[kRevWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t head = blockIdx.x;
   const int n_ent = (int)(n_query * topk);  // < 2^31, checked on the host
@@ -62,6 +70,13 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
   int32_t* out = rev_ent + head * (int64_t)n_ent;
   const int e_beg = wave * segsz;
   const int e_end = min(e_beg + segsz, n_ent);
+  int kres[8];  // RES: the segment (unconditional loads from clamped addresses)
+  if (RES) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) kres[r] = ih[min(e_beg + 64 * r + lane, n_ent - 1)];
+  }
+  const uint64_t below = (1ull << lane) - 1;       // lanes before this one
+  const uint64_t upto = (2ull << lane) - 1;        // ... and this one (all 64 for lane 63)
   int base = 0;
   for (int c0 = 0; c0 < nk; c0 += kRevKeys) {
     const int nc = min(kRevKeys, nk - c0);
@@ -69,9 +84,9 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
     for (int w8 = 0; w8 < kRevWaves; ++w8) cnt[w8][tid] = 0;
     __syncthreads();
     for (int e0 = e_beg; e0 < e_end; e0 += 64 * 8) {
-      int kv[8];  // unconditional loads from clamped addresses: all in flight together
+      int kv[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) kv[r] = ih[min(e0 + 64 * r + lane, n_ent - 1)];
+      for (int r = 0; r < 8; ++r) kv[r] = RES ? kres[r] : ih[min(e0 + 64 * r + lane, n_ent - 1)];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int rel = kv[r] - c0;
@@ -82,16 +97,22 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
     int tot = 0;
 #pragma unroll
     for (int w8 = 0; w8 < kRevWaves; ++w8) tot += cnt[w8][tid];
-    part[tid] = tot;
-    __syncthreads();
-    for (int o = 1; o < kRevKeys; o <<= 1) {
-      const int add = tid >= o ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
+    int incl = tot;  // inclusive scan of the chunk totals across the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
     }
-    const int total = part[kRevKeys - 1];
-    int cur = base + part[tid] - tot;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int pre = 0, total = 0;
+#pragma unroll
+    for (int w8 = 0; w8 < kRevWaves; ++w8) {
+      const int ws = wsum[w8];
+      pre += w8 < wave ? ws : 0;
+      total += ws;
+    }
+    int cur = base + pre + incl - tot;
     if (tid < nc) off[c0 + tid] = cur;
 #pragma unroll
     for (int w8 = 0; w8 < kRevWaves; ++w8) {
@@ -103,30 +124,25 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
     for (int e0 = e_beg; e0 < e_end; e0 += 64 * 8) {
       int kv[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) kv[r] = ih[min(e0 + 64 * r + lane, n_ent - 1)];
+      for (int r = 0; r < 8; ++r) kv[r] = RES ? kres[r] : ih[min(e0 + 64 * r + lane, n_ent - 1)];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        if (e0 + 64 * r >= e_end) break;  // wave-uniform
+        if (e0 + 64 * r >= e_end) break;  // wave-uniform: all 64 lanes take part below
         const int e = e0 + 64 * r + lane;
         const int rel = kv[r] - c0;
         const bool inr = e < e_end && rel >= 0 && rel < nc;
-        const int key = inr ? rel : -1 - lane;  // distinct negatives never match
-        kbuf[wave][lane] = key;
-        int rank = 0;
-        bool later = false;
+        const unsigned key = inr ? (unsigned)rel : (unsigned)kRevKeys;
+        uint64_t same = ~0ull;  // lanes whose key equals this lane's
 #pragma unroll
-        for (int l4 = 0; l4 < 64; l4 += 4) {
-          const int4 k4 = *(const int4*)&kbuf[wave][l4];
-          const int kk4[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool m = kk4[q] == key;
-            rank += (m && l4 + q < lane) ? 1 : 0;
-            later = later || (m && l4 + q > lane);
-          }
+        for (int bit = 0; bit < kRevKeyBits; ++bit) {
+          const bool on = (key >> bit) & 1u;
+          const uint64_t set = __ballot(on);
+          same &= on ? set : ~set;
         }
+        const int rank = __popcll(same & below);
+        const bool later = (same & ~upto) != 0;
         if (inr) out[cnt[wave][rel] + rank] = e;
-        if (inr && !later) cnt[wave][rel] += rank + 1;
+        if (inr && !later) cnt[wave][rel] += rank + 1;  // the last lane of the key advances
       }
     }
     base += total;
@@ -848,8 +864,7 @@ __global__ __launch_bounds__(64) void k_bwd_kv_gen(
 }
 
 template <typename T>
-static hipError_t launch_backward_gen(const LaunchBackward& a, int64_t qtiles, int64_t ktiles,
-                                      bool fork) {
+static hipError_t launch_backward_gen(const LaunchBackward& a, int64_t qtiles, int64_t ktiles) {
   hipError_t err;
   if (qtiles > 0) {
     KernelTimer timer(kKernBackwardQ, a.stream);
@@ -860,7 +875,6 @@ static hipError_t launch_backward_gen(const LaunchBackward& a, int64_t qtiles, i
                        a.n_query, a.n_key, a.S, a.D, a.k, a.dl, a.attn_scale, a.score_scale);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
   if (ktiles > 0) {
     KernelTimer timer(kKernBackwardKV, a.stream);
     auto kern = a.accumulate ? k_bwd_kv_gen<T, true> : k_bwd_kv_gen<T, false>;
@@ -876,24 +890,17 @@ static hipError_t launch_backward_gen(const LaunchBackward& a, int64_t qtiles, i
 hipError_t launch_backward(const LaunchBackward& a) {
   const int64_t heads = a.G * a.B * a.H;
   if (heads == 0) return hipSuccess;
-  // The reverse index is needed only by the key-side kernel: on the side
-  // stream it runs beside the query-side kernel (fork after everything the
-  // caller queued before, join before the key-side kernel).
-  const bool fork = a.side != nullptr;
-  const hipStream_t rs = fork ? a.side : a.stream;
+  // The reverse index first (it needs only idx), then the query-side and the
+  // key-side kernel, all in the caller's stream order.
   hipError_t err;
-  if (fork) {
-    if ((err = hipEventRecord(a.fork, a.stream)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(a.side, a.fork, 0)) != hipSuccess) return err;
-  }
   {
-  KernelTimer timer(kKernReverseIndex, rs);
-  hipLaunchKernelGGL(k_reverse_index, dim3((unsigned)heads), dim3(512), 0, rs, a.idx,
-                     a.n_query, a.n_key, a.k, a.rev_off, a.rev_ent);
+    KernelTimer timer(kKernReverseIndex, a.stream);
+    const bool res = (a.n_query * a.k + kRevWaves - 1) / kRevWaves <= 512;
+    auto kern = res ? k_reverse_index<true> : k_reverse_index<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)heads), dim3(512), 0, a.stream, a.idx, a.n_query,
+                       a.n_key, a.k, a.rev_off, a.rev_ent);
   }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (fork && (err = hipEventRecord(a.join, a.side)) != hipSuccess) return err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
   if (a.dtype == 1 && a.S == 64 && a.D == 64) {
     if (qtiles > 0) {
@@ -906,7 +913,6 @@ hipError_t launch_backward(const LaunchBackward& a) {
                          a.attn_scale, a.score_scale);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (fork && (err = hipStreamWaitEvent(a.stream, a.join, 0)) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
       auto kern = a.accumulate ? k_bwd_kv_bf16<true> : k_bwd_kv_bf16<false>;
@@ -918,10 +924,10 @@ hipError_t launch_backward(const LaunchBackward& a) {
                          a.dl, a.attn_scale, a.score_scale);
     }
   } else if (a.dtype == 1) {
-    err = launch_backward_gen<bf16>(a, qtiles, ktiles, fork);
+    err = launch_backward_gen<bf16>(a, qtiles, ktiles);
     if (err != hipSuccess) return err;
   } else {
-    err = launch_backward_gen<float>(a, qtiles, ktiles, fork);
+    err = launch_backward_gen<float>(a, qtiles, ktiles);
     if (err != hipSuccess) return err;
   }
   return hipGetLastError();

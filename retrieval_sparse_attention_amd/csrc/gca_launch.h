@@ -72,10 +72,6 @@ struct LaunchBackward {
   int32_t* rev_off;  // workspace [heads * (n_key + 1)]
   int32_t* rev_ent;  // workspace [heads * n_query * k]: q * k + slot, grouped by chunk
   hipStream_t stream;
-  // Optional second stream (with two events) on which the reverse index runs
-  // while the query-side kernel runs on `stream`; NULL: everything on `stream`.
-  hipStream_t side;
-  hipEvent_t fork, join;
 };
 
 struct LaunchGather {

@@ -1,7 +1,7 @@
-"""Concurrent callers: gca_backward forks the reverse index onto a stream of the
-library and joins it back with two events shared per device.  Two host threads
-that call the backward at the same time on their own streams (ctypes drops the
-GIL during each call) must each get exactly the bits a lone call gives."""
+"""Concurrent callers: the library keeps no stream, event or lock of its own for
+gca_backward, so two host threads that call the backward at the same time on
+their own streams (ctypes drops the GIL during each call) must each get exactly
+the bits a lone call gives."""
 
 import threading
 

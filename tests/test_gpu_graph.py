@@ -78,9 +78,9 @@ def test_training_step_replays_match_eager():
 
 def test_eager_backward_in_another_thread_during_a_capture():
     """A backward being captured on one thread and an eager backward on another
-    thread's stream at the same time: the captured call runs on its own stream
-    only, so the eager call's fork onto the library's side stream is untouched
-    by the capture.  Replays and the eager call reproduce the reference bits."""
+    thread's stream at the same time: each call enqueues on its own stream only,
+    so the capture holds none of the eager call's work.  Replays and the eager
+    call reproduce the reference bits."""
     name, over = "train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72)
     cfg = synth.workload(name, **over)
     x = synth.training_inputs(name, accept=accept_for(cfg), **over)
