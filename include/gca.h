@@ -29,9 +29,8 @@
  * --------------------------------
  * - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *   never allocates or frees device memory.  Its only state is a thread-local
- *   error string, while enabled the event timing records below, and, per
- *   device, one stream and two events that gca_backward creates on first use
- *   (default priority) and keeps until the process ends.
+ *   error string, while enabled the event timing records below, and the
+ *   fixed device array of gca_retrieve_noalloc.
  * - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *   return without synchronising.
  * - All arrays are dense, contiguous, row-major, with the layouts given below.
@@ -46,6 +45,12 @@
  *   returns GCA_ERR_INVALID_ARGUMENT / GCA_ERR_UNSUPPORTED / GCA_ERR_WORKSPACE,
  *   touches no output and sets gca_last_error().  A failed launch returns
  *   GCA_ERR_DEVICE with the HIP error text in gca_last_error().
+ * - NaN: in gca_forward and gca_backward a NaN in Q, K, V or dO reaches
+ *   every output element that depends on it, in the pattern exact arithmetic
+ *   gives (e.g. a NaN in K of chunk c makes every O and L row of the slots
+ *   that retrieved c NaN; one in V makes one column of those O tiles NaN),
+ *   so a diverging step is not masked.  Retrieval orders finite scores only:
+ *   which chunks a NaN score selects is unspecified.
  * - Setting the environment variable GCA_DEBUG_SYNC=1 makes every call
  *   synchronise its stream and check for device errors before returning.
  *

@@ -189,6 +189,39 @@ def test_bf16_forward_invalid_and_duplicate_slots():
     assert (f64(o)[0, 0, 0, 1] == 0).all()
 
 
+@pytest.mark.parametrize("H,n_query", [(1, 4), (3, 100), (4, 250)],
+                         ids=["4_chunks", "300_chunks", "1000_chunks"])
+def test_bf16_forward_valid_slot_counts(H, n_query):
+    """Rows with every count of valid slots from 0 to 8, the others empty (-1)
+    or out of range, and repeated chunks, at a few query-chunk counts: O and
+    LSE must match the oracle and repeat bit for bit."""
+    n_key = 40
+    cfg = synth.workload("train16k_fwd", B=1, H=H, n_query=n_query, n_key=n_key)
+    rng = np.random.default_rng(H * 1000 + n_query)
+    sc = cfg["value_scale"]
+    mk = lambda *shape: torch.from_numpy(
+        (rng.standard_normal(shape) * sc).astype(np.float32)).bfloat16()
+    q, k, v = mk(1, 1, H, n_query, 64, 64), mk(1, 1, H, n_key, 64, 64), mk(1, 1, H, n_key, 64, 64)
+    idx = rng.integers(0, n_key, size=(1, 1, H, n_query, 8)).astype(np.int32)
+    n_valid = rng.integers(0, 9, size=(1, 1, H, n_query))
+    m = min(9, n_valid.size)
+    n_valid.reshape(-1)[:m] = np.arange(m)
+    for pos in np.ndindex(n_valid.shape):
+        slots = rng.permutation(8)[n_valid[pos]:]
+        idx[pos][slots] = np.where(rng.random(len(slots)) < 0.5, -1, n_key + 3)
+    rep = rng.random(idx.shape[:-1]) < 0.2
+    idx[..., 4][rep] = idx[..., 5][rep]
+    w = rng.random((1, 1, H, n_query, 8)).astype(np.float32)
+    shape = shape_of(cfg)
+    d = [dev(t) for t in (q, k, v, torch.from_numpy(idx), torch.from_numpy(w))]
+    o, lse = run_forward(shape, *d)
+    r_o, r_lse = orc.forward(f64(q), f64(k), f64(v), idx, w.astype(np.float64), cfg["attn_scale"])
+    close("o", f64(o), r_o, True)
+    compare_lse(lse, r_lse, True)
+    o2, lse2 = run_forward(shape, *d)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_bf16_backward_is_deterministic():
     cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=64, n_key=64)
     x = synth.training_inputs("train16k_fwdbwd_g2", accept=accept_for(cfg), G=1, B=1, H=2,
