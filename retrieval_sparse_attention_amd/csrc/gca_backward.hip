@@ -522,22 +522,29 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
   }
 }
 
-// Order in which key chunks go out: chunk-major within groups of kKvHeadGroup
-// consecutive heads (chunk 0 of each head in the group, then chunk 1, ...).
-// A chunk's work grows with its reverse list, and in causal training the
-// early chunks collect the longest lists (about k ln(n/c) entries for chunk
-// c): head after head, the last heads' long lists would start only near the
-// end of the grid and run alone.  Mixing a few heads puts every long list
-// early while the Q/dO tiles in use stay those of a few heads (each XCD works
-// through one contiguous range of this order, see xcd_tile).
-constexpr int64_t kKvHeadGroup = 3;
-
-__device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64_t heads) {
-  const int64_t per = kKvHeadGroup * n_key;
-  const int64_t grp = i / per, within = i % per;
-  const int64_t h0 = grp * kKvHeadGroup;
-  const int64_t gh = heads - h0 < kKvHeadGroup ? heads - h0 : kKvHeadGroup;
-  return (h0 + within % gh) * n_key + within / gh;
+// Order in which key chunks go out.  Each XCD works through one contiguous
+// range of tiles (xcd_tile), head after head, so that the Q/dO tiles in use
+// are those of about one head, which its L2 can nearly hold.  A chunk's work
+// grows with its reverse list, and in causal training the early chunks
+// collect the longest lists (about k ln(n/c) entries for chunk c): in plain
+// head order the range's last heads would start theirs near the end of the
+// grid and run alone.  So the first 32 chunks of the range's last head and
+// the first 8 of the head before it go out first; the rest keep head order.
+__device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64_t nblk) {
+  if (nblk % 8 != 0) return i;  // xcd_tile is the identity then
+  const int64_t R = nblk / 8;
+  const int64_t s0 = (i / R) * R, li = i - s0;  // this XCD's range [s0, s0 + R)
+  const int64_t hl = (s0 + R - 1) / n_key;      // its last head
+  const int64_t b1 = hl * n_key, b2 = (hl - 1) * n_key;
+  int64_t f1 = n_key < 32 ? n_key : 32, f2 = n_key < 8 ? n_key : 8;
+  if (b1 < s0 || b1 + f1 > s0 + R) f1 = 0;  // hoisted blocks lie inside the range
+  if (hl < 1 || b2 < s0) f2 = 0;
+  if (li < f1) return b1 + li;
+  if (li < f1 + f2) return b2 + (li - f1);
+  int64_t t = s0 + (li - f1 - f2);  // the rest in order, skipping both blocks
+  if (f2 && t >= b2) t += f2;
+  if (f1 && t >= b1) t += f1;
+  return t;
 }
 
 // ACC: dk and dv are float32 accumulators that this layer's gradients are
@@ -559,7 +566,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   // = head * n_key + c
-  const int64_t tile = kv_tile_order(xcd_tile(blockIdx.x, gridDim.x), n_key, gridDim.x / n_key);
+  const int64_t tile = kv_tile_order(xcd_tile(blockIdx.x, gridDim.x), n_key, gridDim.x);
   const int64_t head = tile / n_key;
   const int64_t c = tile % n_key;
   const int j = 16 * wave + col;  // key row owned by this lane
