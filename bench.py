@@ -836,10 +836,7 @@ def main():
     for name, (tot, n) in per_kernel.items():
         if n:
             kernels[name] = dict(avg_us=round(tot / n * 1e3, 2), launches=n)
-    if "reverse_index" in kernels:
-        kernels["reverse_index"]["note"] = ("runs on a second stream beside backward_q; its event "
-                                            "time spans that overlap")
-    dom = max((n for n in kernels if n != "reverse_index"),
+    dom = max(kernels,
               key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
     roof = roofline_entry(dom, kernels[dom]["avg_us"] * 1e-6, work[dom])
     sw = step_work(cfg, pairs)
