@@ -202,14 +202,15 @@ __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_
 }
 
 // ---------------------------------------------------------------------------
-// bf16 query-side backward (S = D = 64).  Four waves; wave w owns query rows
-// 16w .. 16w+15 on 16x16x32 MFMA tiles.  The next valid slot's K and V tiles
+// bf16 query-side backward (S = 64, D = 64 or 32).  Four waves; wave w owns
+// query rows 16w .. 16w+15 on 16x16x32 MFMA tiles.  The next valid slot's K and V tiles
 // stream into the other half of a double-buffered swizzled LDS area while the
 // current slot is computed (asynchronous copies the compiler does not wait
 // on; the slot loop is unrolled by two so both buffers are fixed addresses).
 // ---------------------------------------------------------------------------
+template <int D>
 struct BwdQCtx {
-  const TileDma<4>* dma;
+  const TileDma<4, D>* dma;
   const bf16* k_head;
   const bf16* v_head;
   const int* slot_c;   // LDS
@@ -223,16 +224,18 @@ struct BwdQCtx {
   float c2;
 };
 
-__device__ __forceinline__ void bwdq_issue(const BwdQCtx& cx, int u, bf16* __restrict__ kd,
+template <int D>
+__device__ __forceinline__ void bwdq_issue(const BwdQCtx<D>& cx, int u, bf16* __restrict__ kd,
                                            bf16* __restrict__ vd) {
   const int64_t c = uniform(cx.slot_c[uniform(cx.s_list[u])]);
-  cx.dma->copy_async(kd, cx.k_head + c * 4096);
-  cx.dma->copy_async(vd, cx.v_head + c * 4096);
+  cx.dma->copy_async(kd, cx.k_head + c * (64 * D));
+  cx.dma->copy_async(vd, cx.v_head + c * (64 * D));
 }
 
-__device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_next,
-                                          const bf16x8 (&bq)[2], const bf16x8 (&bdo)[2],
-                                          f32x4 (&dqacc)[4], const bf16* __restrict__ kt,
+template <int D>
+__device__ __forceinline__ void bwdq_slot(const BwdQCtx<D>& cx, int u, float& l2_next,
+                                          const bf16x8 (&bq)[D / 32], const bf16x8 (&bdo)[D / 32],
+                                          f32x4 (&dqacc)[D / 16], const bf16* __restrict__ kt,
                                           const bf16* __restrict__ vt, bf16* __restrict__ kn,
                                           bf16* __restrict__ vn) {
   const int lane = cx.lane, grp = cx.grp, col = cx.col;
@@ -256,19 +259,20 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
     sacc[mt] = zero4();
     pacc[mt] = zero4();
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd) {
-      sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
-      pacc[mt] = mfma16x16x32(lds_row8(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
+    for (int kd = 0; kd < D / 32; ++kd) {
+      sacc[mt] = mfma16x16x32(lds_row8<D>(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
+      pacc[mt] = mfma16x16x32(lds_row8<D>(vt, 16 * mt + col, 4 * kd + grp), bdo[kd], pacc[mt]);
     }
   }
   // K^T operands of this slot, requested now so that the LDS latency overlaps
   // the elementwise arithmetic below.
-  bf16x8 ka[2][4];
+  bf16x8 ka[2][D / 16];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      ka[kb][dt] = lds_tr_operand16(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+    for (int dt = 0; dt < D / 16; ++dt)
+      ka[kb][dt] =
+          lds_tr_operand16<D>(kt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
   float dp[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -296,11 +300,11 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx& cx, int u, float& l2_ne
       bs[4 + e] = (bf16)(sacc[2 * kb + 1][e] * (pacc[2 * kb + 1][e] - dsum));
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
+    for (int dt = 0; dt < D / 16; ++dt) dqacc[dt] = mfma16x16x32(ka[kb][dt], bs, dqacc[dt]);
   }
 }
 
-template <bool ACC>
+template <int D, bool ACC>
 __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ lse,
@@ -308,8 +312,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     float* __restrict__ dw_out, float* __restrict__ dscore_out, float* __restrict__ dlq,
     float* __restrict__ delta, float* __restrict__ ds_layer, int64_t n_query, int64_t n_key,
     int topk, int dl, float attn_scale, float score_scale) {
-  __shared__ __align__(16) bf16 k_lds[2][kTileElems];
-  __shared__ __align__(16) bf16 v_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 k_lds[2][64 * D];
+  __shared__ __align__(16) bf16 v_lds[2][64 * D];
   __shared__ float dw_part[4][16];
   __shared__ int slot_c[16];
   __shared__ float slot_w[16];
@@ -345,22 +349,24 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     }
   }
   if (tid < 64) dw_part[tid >> 4][tid & 15] = 0.0f;
-  bf16x8 bq[2], bdo[2];  // Q^T and dO^T as B operands: column x, dims 32kd + 8grp + 0..7
+  bf16x8 bq[D / 32], bdo[D / 32];  // Q^T and dO^T as B operands: column x, dims 32kd + 8grp + 0..7
   {
-    const bf16* qr = q + tile * 4096 + x * 64 + 8 * grp;
-    const bf16* dr = dout + tile * 4096 + x * 64 + 8 * grp;
+    const bf16* qr = q + tile * (64 * D) + x * D + 8 * grp;
+    const bf16* dr = dout + tile * (64 * D) + x * D + 8 * grp;
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd) {
+    for (int kd = 0; kd < D / 32; ++kd) {
       bq[kd] = *(const bf16x8*)(qr + 32 * kd);
       bdo[kd] = *(const bf16x8*)(dr + 32 * kd);
     }
   }
-  f32x4 dqacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  const TileDma<4> dma(wave, lane);
-  BwdQCtx cx;
+  f32x4 dqacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) dqacc[dt] = zero4();
+  const TileDma<4, D> dma(wave, lane);
+  BwdQCtx<D> cx;
   cx.dma = &dma;
-  cx.k_head = kk + head * n_key * 4096;
-  cx.v_head = v + head * n_key * 4096;
+  cx.k_head = kk + head * n_key * (64 * D);
+  cx.v_head = v + head * n_key * (64 * D);
   cx.slot_c = slot_c;
   cx.slot_w = slot_w;
   cx.s_list = s_list;
@@ -386,9 +392,9 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     if (u + 1 < n)
       bwdq_slot(cx, u + 1, l2_next, bq, bdo, dqacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
   }
-  bf16* dqrow = dq + tile * 4096 + x * 64 + 4 * grp;
+  bf16* dqrow = dq + tile * (64 * D) + x * D + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < D / 16; ++dt) {
     bf16x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) val[e] = (bf16)(attn_scale * dqacc[dt][e]);
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 key-side backward (S = D = 64).  Four waves; wave w owns key rows
+// bf16 key-side backward (S = 64, D = 64 or 32).  Four waves; wave w owns key rows
 // 16w .. 16w+15 on 16x16x32 MFMA tiles.  The reverse-list entries are staged
 // in LDS 256 at a time; the next entry's Q and dO tiles stream into the other
 // half of a double-buffered swizzled LDS area (asynchronous copies) and its
@@ -414,10 +420,11 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
 // contraction steps; the entry loop is unrolled by two so both buffers are
 // fixed LDS addresses.
 // ---------------------------------------------------------------------------
+template <int D>
 struct BwdKVCtx {
-  const TileDma<4>* dma;
-  const bf16* q_head;     // q + head * n_query * 4096
-  const bf16* do_head;    // dout + head * n_query * 4096
+  const TileDma<4, D>* dma;
+  const bf16* q_head;     // q + head * n_query * 64 * D
+  const bf16* do_head;    // dout + head * n_query * 64 * D
   const float* lse_head;  // lse + pair0 * 64
   const float* d_head;    // delta + pair0 * 64
   const float* w_head;    // w + pair0
@@ -436,12 +443,13 @@ struct KVNext {
   bf16 lq;
 };
 
-__device__ __forceinline__ void bwdkv_fetch(const BwdKVCtx& cx, int u, KVNext& nx,
+template <int D>
+__device__ __forceinline__ void bwdkv_fetch(const BwdKVCtx<D>& cx, int u, KVNext& nx,
                                             bf16* __restrict__ qd, bf16* __restrict__ dod) {
   const int ent = uniform(cx.s_ent[u]);
   const int t = ent / cx.topk;
-  cx.dma->copy_async(qd, cx.q_head + (int64_t)t * 4096);
-  cx.dma->copy_async(dod, cx.do_head + (int64_t)t * 4096);
+  cx.dma->copy_async(qd, cx.q_head + (int64_t)t * (64 * D));
+  cx.dma->copy_async(dod, cx.do_head + (int64_t)t * (64 * D));
   const int tid = cx.tid;
   if (tid < 128)
     nx.row = tid < 64 ? cx.lse_head[(int64_t)ent * 64 + tid]
@@ -453,10 +461,11 @@ __device__ __forceinline__ void bwdkv_fetch(const BwdKVCtx& cx, int u, KVNext& n
   }
 }
 
-__device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, KVNext& nx,
-                                            float& dlk_acc, const bf16x8 (&bk)[2],
-                                            const bf16x8 (&bv)[2], f32x4 (&dkacc)[4],
-                                            f32x4 (&dvacc)[4], const bf16* __restrict__ qt,
+template <int D>
+__device__ __forceinline__ void bwdkv_entry(const BwdKVCtx<D>& cx, int u, int nb, KVNext& nx,
+                                            float& dlk_acc, const bf16x8 (&bk)[D / 32],
+                                            const bf16x8 (&bv)[D / 32], f32x4 (&dkacc)[D / 16],
+                                            f32x4 (&dvacc)[D / 16], const bf16* __restrict__ qt,
                                             const bf16* __restrict__ dot, float* __restrict__ l2r,
                                             float* __restrict__ dr, bf16* __restrict__ qn,
                                             bf16* __restrict__ don) {
@@ -482,9 +491,9 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
       sacc[h] = zero4();
       pacc[h] = zero4();
 #pragma unroll
-      for (int kd = 0; kd < 2; ++kd) {
-        sacc[h] = mfma16x16x32(lds_row8(qt, xr, 4 * kd + grp), bk[kd], sacc[h]);
-        pacc[h] = mfma16x16x32(lds_row8(dot, xr, 4 * kd + grp), bv[kd], pacc[h]);
+      for (int kd = 0; kd < D / 32; ++kd) {
+        sacc[h] = mfma16x16x32(lds_row8<D>(qt, xr, 4 * kd + grp), bk[kd], sacc[h]);
+        pacc[h] = mfma16x16x32(lds_row8<D>(dot, xr, 4 * kd + grp), bv[kd], pacc[h]);
       }
       // P_w = w P (kept in sacc) and dS = P_w (dP~ - D) (kept in pacc)
       const int x0 = 32 * kb + 16 * h + 4 * grp;
@@ -511,11 +520,11 @@ __device__ __forceinline__ void bwdkv_entry(const BwdKVCtx& cx, int u, int nb, K
     // 128 registers four workgroups share a CU, whose other waves cover the
     // LDS latency.
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       const bf16x8 ado =
-          lds_tr_operand16(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+          lds_tr_operand16<D>(dot, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
       const bf16x8 aq =
-          lds_tr_operand16(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+          lds_tr_operand16<D>(qt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
       dvacc[dt] = mfma16x16x32(ado, bp, dvacc[dt]);
       dkacc[dt] = mfma16x16x32(aq, bs, dkacc[dt]);
     }
@@ -549,7 +558,7 @@ __device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64
 
 // ACC: dk and dv are float32 accumulators that this layer's gradients are
 // added to (in place of bf16 outputs), dlk likewise.
-template <bool ACC>
+template <int D, bool ACC>
 __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const float* __restrict__ w, const float* __restrict__ lse, const bf16* __restrict__ dout,
@@ -558,8 +567,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     const float* __restrict__ dscore, void* __restrict__ dk, void* __restrict__ dv,
     float* __restrict__ dlk, int64_t n_query, int64_t n_key, int topk, int dl,
     float attn_scale, float score_scale) {
-  __shared__ __align__(16) bf16 q_lds[2][kTileElems];
-  __shared__ __align__(16) bf16 do_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 q_lds[2][64 * D];
+  __shared__ __align__(16) bf16 do_lds[2][64 * D];
   __shared__ __align__(16) float l2_lds[2][64];
   __shared__ __align__(16) float d_lds[2][64];
   __shared__ int s_ent[256];
@@ -571,28 +580,29 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
   const int64_t c = tile % n_key;
   const int j = 16 * wave + col;  // key row owned by this lane
 
-  bf16x8 bk[2], bv[2];  // K_c^T and V_c^T as B operands: column j, dims 32kd + 8grp + 0..7
+  bf16x8 bk[D / 32], bv[D / 32];  // K_c^T and V_c^T as B operands: column j, dims 32kd + 8grp + 0..7
   {
-    const bf16* kr = kk + tile * 4096 + j * 64 + 8 * grp;
-    const bf16* vr = v + tile * 4096 + j * 64 + 8 * grp;
+    const bf16* kr = kk + tile * (64 * D) + j * D + 8 * grp;
+    const bf16* vr = v + tile * (64 * D) + j * D + 8 * grp;
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd) {
+    for (int kd = 0; kd < D / 32; ++kd) {
       bk[kd] = *(const bf16x8*)(kr + 32 * kd);
       bv[kd] = *(const bf16x8*)(vr + 32 * kd);
     }
   }
-  f32x4 dkacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  f32x4 dvacc[4] = {zero4(), zero4(), zero4(), zero4()};
+  f32x4 dkacc[D / 16], dvacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) dkacc[dt] = dvacc[dt] = zero4();
   float dlk_acc = 0.0f;
   const int beg = rev_off[head * (n_key + 1) + c];
   const int end = rev_off[head * (n_key + 1) + c + 1];
   const int32_t* ents = rev_ent + head * n_query * topk;
   const int64_t pair0 = head * n_query * topk;
-  const TileDma<4> dma(wave, lane);
-  BwdKVCtx cx;
+  const TileDma<4, D> dma(wave, lane);
+  BwdKVCtx<D> cx;
   cx.dma = &dma;
-  cx.q_head = q + head * n_query * 4096;
-  cx.do_head = dout + head * n_query * 4096;
+  cx.q_head = q + head * n_query * (64 * D);
+  cx.do_head = dout + head * n_query * (64 * D);
   cx.lse_head = lse + pair0 * 64;
   cx.d_head = delta + pair0 * 64;
   cx.w_head = w + pair0;
@@ -622,18 +632,18 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
                     l2_lds[1], d_lds[1], q_lds[0], do_lds[0]);
     }
   }
-  const int64_t orow = tile * 4096 + j * 64 + 4 * grp;
+  const int64_t orow = tile * (64 * D) + j * D + 4 * grp;
   if (ACC) {
     f32x4* dka = (f32x4*)((float*)dk + orow);
     f32x4* dva = (f32x4*)((float*)dv + orow);
-    f32x4 ka[4], va[4];
+    f32x4 ka[D / 16], va[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       ka[dt] = dka[4 * dt];
       va[dt] = dva[4 * dt];
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ka[dt][e] += attn_scale * dkacc[dt][e];
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_kv_bf16(
     bf16* dkrow = (bf16*)dk + orow;
     bf16* dvrow = (bf16*)dv + orow;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt) {
       bf16x4 kv4, vv4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -909,10 +919,11 @@ hipError_t launch_backward(const LaunchBackward& a) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
-  if (a.dtype == 1 && a.S == 64 && a.D == 64) {
+  if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
     if (qtiles > 0) {
       KernelTimer timer(kKernBackwardQ, a.stream);
-      auto kern = a.accumulate ? k_bwd_q_bf16<true> : k_bwd_q_bf16<false>;
+      auto kern = a.D == 64 ? (a.accumulate ? k_bwd_q_bf16<64, true> : k_bwd_q_bf16<64, false>)
+                            : (a.accumulate ? k_bwd_q_bf16<32, true> : k_bwd_q_bf16<32, false>);
       hipLaunchKernelGGL(kern, dim3((unsigned)qtiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
                          a.lse, (const bf16*)a.dout, (const bf16*)a.lk, (bf16*)a.dq, a.dw,
@@ -922,7 +933,8 @@ hipError_t launch_backward(const LaunchBackward& a) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ktiles > 0) {
       KernelTimer timer(kKernBackwardKV, a.stream);
-      auto kern = a.accumulate ? k_bwd_kv_bf16<true> : k_bwd_kv_bf16<false>;
+      auto kern = a.D == 64 ? (a.accumulate ? k_bwd_kv_bf16<64, true> : k_bwd_kv_bf16<64, false>)
+                            : (a.accumulate ? k_bwd_kv_bf16<32, true> : k_bwd_kv_bf16<32, false>);
       hipLaunchKernelGGL(kern, dim3((unsigned)ktiles), dim3(256), 0, a.stream,
                          (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.w, a.lse,
                          (const bf16*)a.dout, a.delta, a.rev_off, a.rev_ent, (const bf16*)a.lq,

@@ -154,14 +154,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// LDS tiles: 64 rows x 64 bf16 with 128-byte rows, XOR-swizzled at 16-byte
-// granularity: chunk c (columns 8c .. 8c+7) of row r sits at chunk position
-// c ^ (r & 7).  Eight consecutive rows reading the same logical chunk, and the
-// 4-row x 16-column blocks of the transpose read, then hit distinct banks.
+// LDS tiles: 64 rows x D bf16 (D = 64: 128-byte rows; D = 32: 64-byte rows),
+// XOR-swizzled at 16-byte granularity: chunk c (columns 8c .. 8c+7) of row r
+// sits at chunk position c ^ (r mod D/8).  Consecutive rows reading the same
+// logical chunk, and the 4-row x 16-column blocks of the transpose read, then
+// hit distinct banks.
 constexpr int kTileElems = 64 * 64;
 
+template <int D = 64>
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+  static_assert(D == 32 || D == 64, "tile rows of 32 or 64 elements");
+  return row * D + ((((col >> 3) ^ (row & (D / 8 - 1)))) << 3) + (col & 7);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -184,24 +187,28 @@ __device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* __restrict_
 }
 
 // The same copy with the per-lane part of the addresses computed once: `off`
-// holds, for each of the wave's 8/NW pieces, this lane's byte offset inside
-// the source tile, so a copy costs no vector arithmetic when the tile base is
-// wave-uniform (it is then used as the scalar base of global_load_lds).
-template <int NW>
+// holds, for each of the wave's pieces (1 KB each: 64 x D tiles have D/8 of
+// them, shared by NW waves), this lane's byte offset inside the source tile, so
+// a copy costs no vector arithmetic when the tile base is wave-uniform (it is
+// then used as the scalar base of global_load_lds).
+template <int NW, int D = 64>
 struct TileDma {
-  uint32_t off[8 / NW];
+  static constexpr int kPieces = D / 8 / NW;  // per wave
+  static constexpr int kRows = 512 / D;       // tile rows per piece
+  static constexpr int kChunks = D / 8;       // 16-byte chunks per row
+  uint32_t off[kPieces];
   int first_piece;
-  __device__ __forceinline__ TileDma(int wave, int lane) : first_piece(wave * (8 / NW)) {
+  __device__ __forceinline__ TileDma(int wave, int lane) : first_piece(wave * kPieces) {
 #pragma unroll
-    for (int r = 0; r < 8 / NW; ++r) {
-      const int row = (first_piece + r) * 8 + (lane >> 3), pc = lane & 7;
-      off[r] = (uint32_t)(row * 64 + ((pc ^ (row & 7)) << 3)) * 2u;
+    for (int r = 0; r < kPieces; ++r) {
+      const int row = (first_piece + r) * kRows + lane / kChunks, pc = lane % kChunks;
+      off[r] = (uint32_t)(row * D + ((pc ^ (row & (kChunks - 1))) << 3)) * 2u;
     }
   }
   __device__ __forceinline__ void copy(bf16* lds_tile, const bf16* src) const {
     const char* base = (const char*)src;
 #pragma unroll
-    for (int r = 0; r < 8 / NW; ++r)
+    for (int r = 0; r < kPieces; ++r)
       __builtin_amdgcn_global_load_lds((const void*)(base + off[r]),
                                        (lds_void*)(lds_tile + (first_piece + r) * 512), 16, 0, 0);
   }
@@ -214,7 +221,7 @@ struct TileDma {
   __device__ __forceinline__ void copy_async(bf16* lds_tile, const bf16* src) const {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds_tile;
 #pragma unroll
-    for (int r = 0; r < 8 / NW; ++r) {
+    for (int r = 0; r < kPieces; ++r) {
       const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
           (int)(lds0 + (uint32_t)(first_piece + r) * 1024u));
       uint32_t saved;
@@ -251,8 +258,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // 16-byte read of row `row`, logical chunk `chunk` of a swizzled tile.
+template <int D = 64>
 __device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int row, int chunk) {
-  return *(const bf16x8*)(tile + swz(row, 8 * chunk));
+  return *(const bf16x8*)(tile + swz<D>(row, 8 * chunk));
 }
 
 // gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
@@ -282,12 +290,13 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* tile, int c_base, i
 // Operand for a 16x16x32 MFMA whose lane owns column (c_base + lane % 16) of a
 // swizzled LDS tile and whose 8 contraction values are the tile rows
 // r_a .. r_a+3 and r_b .. r_b+3 (picked per 16-lane group by the caller).
+template <int D = 64>
 __device__ __forceinline__ bf16x8 lds_tr_operand16(const bf16* tile, int c_base, int r_a, int r_b,
                                                    int lane) {
   const int s = lane & 15;
   const int col = c_base + 4 * (s & 3);
-  const bf16x4 a = lds_read_tr(tile + swz(r_a + (s >> 2), col));
-  const bf16x4 b = lds_read_tr(tile + swz(r_b + (s >> 2), col));
+  const bf16x4 a = lds_read_tr(tile + swz<D>(r_a + (s >> 2), col));
+  const bf16x4 b = lds_read_tr(tile + swz<D>(r_b + (s >> 2), col));
   bf16x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];

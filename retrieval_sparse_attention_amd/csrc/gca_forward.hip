@@ -5,10 +5,11 @@
 // separately to the S tokens of each retrieved chunk c_i, giving O^i[x] and the
 // log-sum-exp L_i[x]; the output is O[x] = sum_i w_i O^i[x].
 //
-// bf16 path (S = D = 64).  One workgroup of four waves per query chunk; wave w
-// owns query rows 16w .. 16w+15 and works on 16x16x32 MFMA tiles.  Per
+// bf16 path (S = 64, D = 64 or 32).  One workgroup of four waves per query
+// chunk; wave w owns query rows 16w .. 16w+15 and works on 16x16x32 MFMA
+// tiles (D/32 contraction steps for the scores, D/16 column tiles of O).  Per
 // retrieved chunk:
-//   1. the K and V tiles (8 KB each) of the next retrieved chunk stream from
+//   1. the K and V tiles (2D bytes per row) of the next retrieved chunk stream from
 //      global memory straight into the other half of a double-buffered,
 //      XOR-swizzled LDS area (global_load_lds, scalar tile base plus per-lane
 //      offsets computed once) while the current chunk is computed; one barrier
@@ -35,8 +36,9 @@
 namespace gca {
 
 // Per-workgroup state of the bf16 forward shared by its chunk steps.
+template <int D>
 struct FwdCtx {
-  const TileDma<4>* dma;
+  const TileDma<4, D>* dma;
   const bf16* k_head;
   const bf16* v_head;
   const int* s_c;      // LDS: chunk of each valid slot
@@ -49,19 +51,21 @@ struct FwdCtx {
 };
 
 // DMA of the K and V tiles of valid slot u into kd / vd.
-__device__ __forceinline__ void fwd_issue(const FwdCtx& cx, int u, bf16* __restrict__ kd,
+template <int D>
+__device__ __forceinline__ void fwd_issue(const FwdCtx<D>& cx, int u, bf16* __restrict__ kd,
                                           bf16* __restrict__ vd) {
   const int64_t c = uniform(cx.s_c[u]);
-  cx.dma->copy_async(kd, cx.k_head + c * 4096);
-  cx.dma->copy_async(vd, cx.v_head + c * 4096);
+  cx.dma->copy_async(kd, cx.k_head + c * (64 * D));
+  cx.dma->copy_async(vd, cx.v_head + c * (64 * D));
 }
 
 // One retrieved chunk: kt/vt hold its tiles; the next chunk's tiles are sent
 // to kn/vn.  The restrict qualifiers tell the compiler that the LDS reads of
 // this chunk never touch the buffers being filled, so it does not wait for
 // that copy before reading (it would otherwise drain the copy at once).
-__device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 (&bq)[2],
-                                          f32x4 (&oacc)[4], const bf16* __restrict__ kt,
+template <int D>
+__device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, const bf16x8 (&bq)[D / 32],
+                                          f32x4 (&oacc)[D / 16], const bf16* __restrict__ kt,
                                           const bf16* __restrict__ vt, bf16* __restrict__ kn,
                                           bf16* __restrict__ vn) {
   const int lane = cx.lane, grp = cx.grp, col = cx.col;
@@ -75,17 +79,18 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
   for (int mt = 0; mt < 4; ++mt) {
     sacc[mt] = zero4();
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd)
-      sacc[mt] = mfma16x16x32(lds_row8(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
+    for (int kd = 0; kd < D / 32; ++kd)
+      sacc[mt] = mfma16x16x32(lds_row8<D>(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
   }
   // V^T operands of this slot, requested now so that the LDS latency overlaps
   // the softmax arithmetic below.
-  bf16x8 va[2][4];
+  bf16x8 va[2][D / 16];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      va[kb][dt] = lds_tr_operand16(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+    for (int dt = 0; dt < D / 16; ++dt)
+      va[kb][dt] =
+          lds_tr_operand16<D>(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
   float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
 #pragma unroll
   for (int r = 1; r < 4; ++r)
@@ -103,7 +108,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
-  f32x4 pv[4], lacc = zero4();
+  f32x4 pv[D / 16], lacc = zero4();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     bf16x8 bp;
@@ -113,7 +118,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
       bp[4 + e] = (bf16)sacc[2 * kb + 1][e];
     }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) pv[dt] = mfma16x16x32(va[kb][dt], bp, kb ? pv[dt] : zero4());
+    for (int dt = 0; dt < D / 16; ++dt) pv[dt] = mfma16x16x32(va[kb][dt], bp, kb ? pv[dt] : zero4());
     lacc = mfma16x16x32(ones, bp, lacc);
   }
   const float l = lacc[0];
@@ -121,17 +126,18 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx& cx, int u, const bf16x8 
   // O^T += (w_i / l) V^T P^T: the fusion weight and the normalisation in one factor
   const float ps = cx.s_w[u] * fast_rcp(l);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(ps, pv[dt][e], oacc[dt][e]);
 }
 
-__global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
+template <int D>
+__global__ __launch_bounds__(256) void k_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ o,
     float* __restrict__ lse, int64_t n_query, int64_t n_key, int topk, float attn_scale) {
-  __shared__ __align__(16) bf16 k_lds[2][kTileElems];
-  __shared__ __align__(16) bf16 v_lds[2][kTileElems];
+  __shared__ __align__(16) bf16 k_lds[2][64 * D];
+  __shared__ __align__(16) bf16 v_lds[2][64 * D];
   __shared__ int s_c[16];
   __shared__ float s_w[16];
   __shared__ int s_slot[16];
@@ -165,18 +171,20 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
       s_mask = (int)mask;
     }
   }
-  bf16x8 bq[2];  // Q^T as the B operand: column x, dims 32*kd + 8*grp + 0..7
+  bf16x8 bq[D / 32];  // Q^T as the B operand: column x, dims 32*kd + 8*grp + 0..7
   {
-    const bf16* row = q + tile * 4096 + x * 64 + 8 * grp;
+    const bf16* row = q + tile * (64 * D) + x * D + 8 * grp;
 #pragma unroll
-    for (int kd = 0; kd < 2; ++kd) bq[kd] = *(const bf16x8*)(row + 32 * kd);
+    for (int kd = 0; kd < D / 32; ++kd) bq[kd] = *(const bf16x8*)(row + 32 * kd);
   }
-  f32x4 oacc[4] = {zero4(), zero4(), zero4(), zero4()};
-  const TileDma<4> dma(wave, lane);
-  FwdCtx cx;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = zero4();
+  const TileDma<4, D> dma(wave, lane);
+  FwdCtx<D> cx;
   cx.dma = &dma;
-  cx.k_head = kk + head * n_key * 4096;
-  cx.v_head = v + head * n_key * 4096;
+  cx.k_head = kk + head * n_key * (64 * D);
+  cx.v_head = v + head * n_key * (64 * D);
   cx.s_c = s_c;
   cx.s_w = s_w;
   cx.s_slot = s_slot;
@@ -201,9 +209,9 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s64d64(
     for (int e = tid; e < topk * 64; e += 256) lse[tile * topk * 64 + e] = s_lse[e];
   }
   // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
-  bf16* orow = o + tile * 4096 + x * 64 + 4 * grp;
+  bf16* orow = o + tile * (64 * D) + x * D + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < D / 16; ++dt) {
     bf16x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) val[e] = (bf16)oacc[dt][e];
@@ -285,10 +293,11 @@ hipError_t launch_forward(const LaunchForward& a) {
   const int64_t tiles = a.G * a.B * a.H * a.n_query;
   if (tiles == 0) return hipSuccess;
   KernelTimer timer(kKernForward, a.stream);
-  if (a.dtype == 1 && a.S == 64 && a.D == 64) {
-    hipLaunchKernelGGL(k_fwd_bf16_s64d64, dim3((unsigned)tiles), dim3(256), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,
-                       (bf16*)a.o, a.lse, a.n_query, a.n_key, a.k, a.attn_scale);
+  if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
+    auto kern = a.D == 64 ? k_fwd_bf16<64> : k_fwd_bf16<32>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), 0, a.stream, (const bf16*)a.q,
+                       (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w, (bf16*)a.o, a.lse,
+                       a.n_query, a.n_key, a.k, a.attn_scale);
   } else if (a.dtype == 1) {
     hipLaunchKernelGGL(k_fwd_gen<bf16>, dim3((unsigned)tiles), dim3(64), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w,

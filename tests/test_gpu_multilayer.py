@@ -78,9 +78,10 @@ def _oracle_group(cfg, base, layers, r_idx, r_w):
 
 @pytest.mark.parametrize("name,over", [
     ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72)),
+    ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72, D=32)),
     ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=40, n_key=40, S=16, D=32)),
     ("tiny_fp32", dict(H=3)),
-], ids=["bf16", "bf16_s16_d32", "fp32"])
+], ids=["bf16", "bf16_d32", "bf16_s16_d32", "fp32"])
 def test_one_retrieval_three_layers_accumulate(name, over):
     L = 3
     cfg, base, layers = _layers(name, L, **over)

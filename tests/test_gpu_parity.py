@@ -80,9 +80,16 @@ def test_bf16_top_k_sizes(k):
 
 @pytest.mark.parametrize("S,D", [(16, 32), (16, 64), (64, 32), (5, 7)])
 def test_bf16_chunk_and_head_sizes(S, D):
-    # bf16 attention beyond 64 x 64 tiles (the float32 VALU path): every output
-    # of retrieve -> forward -> backward against the oracle, two groups
+    # bf16 attention at other sizes (64 x 32: the MFMA kernels with half-width
+    # rows; the rest: the float32 VALU path): every output of retrieve ->
+    # forward -> backward against the oracle, two groups
     _full_path("train16k_fwdbwd_g2", B=1, H=2, n_query=40, n_key=40, S=S, D=D)
+
+
+def test_bf16_head_dim_32_mfma_multiple_tiles():
+    # the 64 x 32 MFMA kernels over enough query and key chunks for several
+    # tiles per XCD and reverse lists past one block: a 3-head training shape
+    _full_path("train16k_fwdbwd_g2", G=1, B=1, H=3, n_query=160, n_key=160, D=32)
 
 
 def test_bf16_landmark_dim_32():
