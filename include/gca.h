@@ -57,10 +57,10 @@
  * Supported sizes (anything else returns GCA_ERR_UNSUPPORTED):
  *   dtype GCA_BF16 : chunk_size 1..64, head_dim 1..64, landmark_dim 32 or 64
  *                    (gca_forward / gca_backward run MFMA kernels at
- *                    chunk_size 64, the pages' chunk size, with head_dim 64
- *                    or 32; other sizes take a float32 VALU path with bf16
- *                    loads and one rounding of each output, correct but
- *                    about two orders of magnitude slower)
+ *                    chunk_size 64, the pages' chunk size, and 16, each with
+ *                    head_dim 64 or 32; other sizes take a float32 VALU path
+ *                    with bf16 loads and one rounding of each output, correct
+ *                    but about two orders of magnitude slower)
  *   dtype GCA_F32  : chunk_size 1..64, head_dim 1..64, landmark_dim 1..128
  *   top_k 1..16; n_key < 2^31 - 1; at most 2^31 - 1 query or key chunk tiles
  *   (G*B*H*n_query, G*B*H*n_key); gca_backward needs n_query * top_k < 2^31.
@@ -300,7 +300,7 @@ gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const voi
  *   lse   [G, B, H, Nq, k, S]  float32 output, may be NULL (then not written;
  *                              gca_backward needs it)
  *
- * With dtype GCA_BF16, chunk_size 64 and head_dim 64 or 32, attn_scale must be >= 0
+ * With dtype GCA_BF16, chunk_size 64 or 16 and head_dim 64 or 32, attn_scale must be >= 0
  * (else GCA_ERR_UNSUPPORTED): those kernels subtract each row's largest unscaled
  * product before exponentiating, which bounds the exponents only for a
  * non-negative scale.

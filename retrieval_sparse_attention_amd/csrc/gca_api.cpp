@@ -480,13 +480,13 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, con
                        const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
   Sizes z;
   GCA_TRY(check_shape(shape, kForward, &z));
-  // the bf16 MFMA kernels (64-row tiles, head_dim 64 or 32) shift by the
+  // the bf16 MFMA kernels (chunk_size 64 or 16, head_dim 64 or 32) shift by the
   // largest unscaled product: a bound on the exponents only for a
   // non-negative scale
-  if (shape->dtype == GCA_BF16 && shape->chunk_size == 64 &&
+  if (shape->dtype == GCA_BF16 && (shape->chunk_size == 64 || shape->chunk_size == 16) &&
       (shape->head_dim == 64 || shape->head_dim == 32) && shape->attn_scale < 0.0f)
     return fail(GCA_ERR_UNSUPPORTED,
-                "gca_forward: bf16 attention on 64-row MFMA tiles needs attn_scale >= 0");
+                "gca_forward: bf16 attention on MFMA tiles needs attn_scale >= 0");
   if (z.q_rows == 0) {
     g_err[0] = '\0';
     return GCA_OK;

@@ -155,13 +155,6 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
 // dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq (ACC:
 // adds them to the float32 accumulators instead).  With no resident chunk
 // (lk_head null) every slot is empty and dlq is 0.
-template <bool ACC>
-__device__ __forceinline__ void put(float* p, float v) {
-  if (ACC)
-    *p += v;
-  else
-    *p = v;
-}
 
 template <typename LT, bool ACC>
 __device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_c,
@@ -919,7 +912,10 @@ hipError_t launch_backward(const LaunchBackward& a) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t qtiles = heads * a.n_query, ktiles = heads * a.n_key;
-  if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
+  if (a.dtype == 1 && a.S == 16 && (a.D == 64 || a.D == 32)) {
+    err = launch_backward_s16(a, qtiles, ktiles);
+    if (err != hipSuccess) return err;
+  } else if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
     if (qtiles > 0) {
       KernelTimer timer(kKernBackwardQ, a.stream);
       auto kern = a.D == 64 ? (a.accumulate ? k_bwd_q_bf16<64, true> : k_bwd_q_bf16<64, false>)

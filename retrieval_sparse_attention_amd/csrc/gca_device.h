@@ -187,13 +187,14 @@ __device__ __forceinline__ void tile_dma(bf16* lds_tile, const bf16* __restrict_
 }
 
 // The same copy with the per-lane part of the addresses computed once: `off`
-// holds, for each of the wave's pieces (1 KB each: 64 x D tiles have D/8 of
-// them, shared by NW waves), this lane's byte offset inside the source tile, so
+// holds, for each of the wave's pieces (1 KB each: ROWS x D tiles have
+// ROWS * D / 512 of them, shared by NW waves), this lane's byte offset inside
+// the source tile, so
 // a copy costs no vector arithmetic when the tile base is wave-uniform (it is
 // then used as the scalar base of global_load_lds).
-template <int NW, int D = 64>
+template <int NW, int D = 64, int ROWS = 64>
 struct TileDma {
-  static constexpr int kPieces = D / 8 / NW;  // per wave
+  static constexpr int kPieces = ROWS * D / 512 / NW;  // per wave
   static constexpr int kRows = 512 / D;       // tile rows per piece
   static constexpr int kChunks = D / 8;       // 16-byte chunks per row
   uint32_t off[kPieces];
@@ -303,6 +304,15 @@ __device__ __forceinline__ bf16x8 lds_tr_operand16(const bf16* tile, int c_base,
   return r;
 }
 
+
+// Output write: stored, or (ACC) added to a float32 accumulator.
+template <bool ACC>
+__device__ __forceinline__ void put(float* p, float v) {
+  if (ACC)
+    *p += v;
+  else
+    *p = v;
+}
 
 __device__ __forceinline__ float load_f(const float* p) { return *p; }
 __device__ __forceinline__ float load_f(const bf16* p) { return (float)(*p); }

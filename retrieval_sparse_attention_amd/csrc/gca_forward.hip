@@ -293,7 +293,9 @@ hipError_t launch_forward(const LaunchForward& a) {
   const int64_t tiles = a.G * a.B * a.H * a.n_query;
   if (tiles == 0) return hipSuccess;
   KernelTimer timer(kKernForward, a.stream);
-  if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
+  if (a.dtype == 1 && a.S == 16 && (a.D == 64 || a.D == 32)) {
+    return launch_forward_s16(a, tiles);
+  } else if (a.dtype == 1 && a.S == 64 && (a.D == 64 || a.D == 32)) {
     auto kern = a.D == 64 ? k_fwd_bf16<64> : k_fwd_bf16<32>;
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), 0, a.stream, (const bf16*)a.q,
                        (const bf16*)a.kk, (const bf16*)a.v, a.idx, a.w, (bf16*)a.o, a.lse,

@@ -83,14 +83,15 @@ def test_bf16_attention_sizes():
         bad = _bf16_shape(chunk_size=S, head_dim=D)
         st, msg = _status("gca_workspace_size", ctypes.byref(bad), 1, ctypes.byref(n))
         assert st == 2 and "<= 64" in msg
-    # the non-negative scale condition holds only for the MFMA forwards (64-row
-    # tiles, head_dim 64 or 32)
-    s = _bf16_shape(chunk_size=16, head_dim=32, attn_scale=-0.5)
+    # the non-negative scale condition holds only for the MFMA forwards
+    # (chunk_size 64 or 16, head_dim 64 or 32)
+    s = _bf16_shape(chunk_size=5, head_dim=7, attn_scale=-0.5)
     st, msg = _status("gca_forward", ctypes.byref(s), None, A, A, A, A, A, None, None)
     assert st == 1 and "q is NULL" in msg
-    s = _bf16_shape(chunk_size=64, head_dim=32, attn_scale=-0.5)
-    st, msg = _status("gca_forward", ctypes.byref(s), A, A, A, A, A, A, None, None)
-    assert st == 2 and "attn_scale >= 0" in msg
+    for S, D in ((64, 32), (16, 64), (16, 32)):
+        s = _bf16_shape(chunk_size=S, head_dim=D, attn_scale=-0.5)
+        st, msg = _status("gca_forward", ctypes.byref(s), A, A, A, A, A, A, None, None)
+        assert st == 2 and "attn_scale >= 0" in msg
 
 
 def test_f32_limits():

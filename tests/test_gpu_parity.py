@@ -81,9 +81,18 @@ def test_bf16_top_k_sizes(k):
 @pytest.mark.parametrize("S,D", [(16, 32), (16, 64), (64, 32), (5, 7)])
 def test_bf16_chunk_and_head_sizes(S, D):
     # bf16 attention at other sizes (64 x 32: the MFMA kernels with half-width
-    # rows; the rest: the float32 VALU path): every output of retrieve ->
-    # forward -> backward against the oracle, two groups
+    # rows; 16 x 64 and 16 x 32: the one-wave-per-chunk MFMA kernels; 5 x 7:
+    # the float32 VALU path): every output of retrieve -> forward -> backward
+    # against the oracle, two groups
     _full_path("train16k_fwdbwd_g2", B=1, H=2, n_query=40, n_key=40, S=S, D=D)
+
+
+@pytest.mark.parametrize("D", [64, 32])
+def test_bf16_chunk_16_ragged_workgroups(D):
+    # the 16-token kernels run four chunks per workgroup: 3 heads x 161 chunks
+    # leave the last workgroup with one busy wave on each side, and reverse
+    # lists run past one 64-entry block
+    _full_path("train16k_fwdbwd_g2", G=1, B=1, H=3, n_query=161, n_key=161, S=16, D=D)
 
 
 def test_bf16_head_dim_32_mfma_multiple_tiles():

@@ -56,8 +56,9 @@ def _expected_lists(idx_head, n_key):
 @pytest.mark.parametrize("n_query,n_key,S,D,heavy", [
     (40, 700, 64, 64, False),      # index segments held in registers, two passes
     (520, 1100, 64, 64, True),     # segments re-read, three passes, a 520-entry list
-    (24, 600, 16, 32, True),       # the generic key-side kernel, two passes
-], ids=["two_passes", "three_passes_heavy", "generic_s16_d32"])
+    (24, 600, 16, 32, True),       # the 16-token key-side kernel, two passes
+    (24, 600, 5, 7, True),         # the generic key-side kernel, two passes
+], ids=["two_passes", "three_passes_heavy", "s16_d32", "generic_s5_d7"])
 def test_reverse_lists_and_gradients(n_query, n_key, S, D, heavy):
     H, k = 2, 8
     over = dict(G=1, B=1, H=H, n_query=n_query, n_key=n_key, S=S, D=D)
