@@ -32,13 +32,13 @@ def _gpu():
     require_gpu()
 
 
-def _inputs(seed):
-    cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=1, n_query=NQ, n_key=NK)
+def _inputs(seed, S=64, D=64):
+    cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=1, n_query=NQ, n_key=NK, S=S, D=D)
     rng = np.random.default_rng(seed)
     sc = cfg["value_scale"]
     mk = lambda *s: (rng.standard_normal(s) * sc).astype(np.float32)
-    x = dict(q=mk(1, 1, 1, NQ, 64, 64), k=mk(1, 1, 1, NK, 64, 64), v=mk(1, 1, 1, NK, 64, 64),
-             dout=mk(1, 1, 1, NQ, 64, 64), lq=mk(1, 1, 1, NQ, 64), lk=mk(1, 1, 1, NK, 64))
+    x = dict(q=mk(1, 1, 1, NQ, S, D), k=mk(1, 1, 1, NK, S, D), v=mk(1, 1, 1, NK, S, D),
+             dout=mk(1, 1, 1, NQ, S, D), lq=mk(1, 1, 1, NQ, 64), lk=mk(1, 1, 1, NK, 64))
     # query chunk t retrieves chunks t, t+1, t+2, t+3 (chunk 2 by t = 0, 1, 2)
     idx = np.full((1, 1, 1, NQ, 8), -1, np.int32)
     for t in range(NQ):
@@ -63,10 +63,15 @@ def _same_nan_pattern(name, got, ref):
     close(name, got, ref, True, mask=np.isfinite(ref))
 
 
+# the 64-token MFMA kernels, the 16-token ones and the half-width rows
+SIZES = [(64, 64), (16, 64), (16, 32)]
+
+
+@pytest.mark.parametrize("S,D", SIZES, ids=["s64_d64", "s16_d64", "s16_d32"])
 @pytest.mark.parametrize("where", ["q", "k", "v"])
-def test_forward_nan_reaches_its_outputs(where):
-    cfg, x, idx, w = _inputs(5)
-    pos = {"q": (0, 0, 0, 1, 7, 3), "k": (0, 0, 0, 2, 11, 40), "v": (0, 0, 0, 2, 11, 40)}[where]
+def test_forward_nan_reaches_its_outputs(where, S, D):
+    cfg, x, idx, w = _inputs(5, S, D)
+    pos = {"q": (0, 0, 0, 1, 7, 3), "k": (0, 0, 0, 2, 11, 20), "v": (0, 0, 0, 2, 11, 20)}[where]
     x[where][pos] = np.nan
     t = {key: _bf16(x[key]) for key in ("q", "k", "v")}
     shape = shape_of(cfg)
@@ -79,9 +84,10 @@ def test_forward_nan_reaches_its_outputs(where):
         _same_nan_pattern("lse", f64(lse), r_lse)
 
 
-def test_backward_nan_in_dout_reaches_its_gradients():
-    cfg, x, idx, w = _inputs(6)
-    x["dout"][0, 0, 0, 3, 20, 5] = np.nan
+@pytest.mark.parametrize("S,D", SIZES, ids=["s64_d64", "s16_d64", "s16_d32"])
+def test_backward_nan_in_dout_reaches_its_gradients(S, D):
+    cfg, x, idx, w = _inputs(6, S, D)
+    x["dout"][0, 0, 0, 3, 12, 5] = np.nan
     t = {key: _bf16(x[key]) for key in ("q", "k", "v", "dout", "lq", "lk")}
     shape = shape_of(cfg)
     d = {key: dev(val) for key, val in t.items()}
