@@ -39,7 +39,8 @@ def parse():
                     help="skip the 16M-token retrieval and 1M-token inference measurements")
     ap.add_argument("--infer-steps", type=int, default=1000)
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the cold-cache step, the copy rate and the one-group forward")
+                    help="skip the cold-cache step, the copy rate, the one-group forward and "
+                         "the step at the other tile sizes")
     ap.add_argument("--no-swa", action="store_true",
                     help="skip the sliding-window self-attention step")
     ap.add_argument("--no-gumbel", action="store_true",
@@ -426,6 +427,58 @@ def bench_train16k_fwd(steps, x=None):
             "forward_TFLOPs": round(wk["flops"] / fwd_s / 1e12, 1) if fwd_s else None,
             "forward_roofline_us": round(t_roof * 1e6, 2),
             "forward_roofline_frac": round(t_roof / fwd_s, 4) if fwd_s else None}
+
+
+def bench_tile_sizes(steps):
+    """The training step of the headline workload (retrieve + forward + backward, G=2, B=4,
+    H=12, 16K tokens, k=8, off-by-one weights) at the other bf16 tile sizes that run on
+    MFMA kernels: 64-token chunks with head_dim 32, and 16-token chunks with head_dim 64
+    and 32 (n = 16384 / S chunks per head).  Tokens per step count B * 16K, as in the
+    headline."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    import synth
+    out = {}
+    for S, D in ((64, 32), (16, 64), (16, 32)):
+        n = 16384 // S
+        over = dict(S=S, D=D, n_query=n, n_key=n)
+        cfg = synth.workload(WORKLOAD, **over)
+        x = synth.training_inputs(WORKLOAD, **over)
+        d = {key: val.contiguous().cuda() for key, val in x.items() if key != "cfg"}
+        del x
+        G, B, H, k, Dl = cfg["G"], cfg["B"], cfg["H"], cfg["k"], cfg["Dl"]
+        shape = gca.make_shape(G, B, H, n, n, S, D, Dl, k, gca.GCA_BF16, cfg["softmax_one"])
+        idx = torch.empty((G, B, H, n, k), dtype=torch.int32, device="cuda")
+        score = torch.empty((G, B, H, n, k), device="cuda")
+        w = torch.empty_like(score)
+        o = torch.empty_like(d["q"])
+        lse = torch.empty((G, B, H, n, k, S), device="cuda")
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        dw, dscore = torch.empty_like(w), torch.empty_like(w)
+        dlq = torch.empty(tuple(d["lq"].shape), device="cuda")
+        dlk = torch.empty(tuple(d["lk"].shape), device="cuda")
+        wsr = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)),
+                          dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(gca.gca_workspace_size(shape, gca.OP_BACKWARD), dtype=torch.uint8,
+                          device="cuda")
+
+        def step():
+            gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], idx, score, w, ws=wsr)
+            gca.gca_forward(shape, d["q"], d["k"], d["v"], idx, w, o, lse)
+            gca.gca_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"],
+                             d["lk"], dq, dk, dv, dw, dscore, dlq, dlk, ws=wsb)
+
+        for _ in range(3):
+            step()
+        ms, per = _timed(step, steps)
+        out[f"S{S}_D{D}"] = {"chunk_size": S, "head_dim": D, "chunks_per_head": n,
+                             "ms_per_step": round(ms, 4),
+                             "tokens_per_s": round(B * n * S / (ms / 1e3), 1),
+                             "kernels_us": {kn: round(v * 1e3, 2) for kn, v in per.items()}}
+        del d, o, lse, dq, dk, dv, wsr, wsb
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_cold_and_copy(step, reps=5):
@@ -875,7 +928,7 @@ def main():
         swa_res = bench_swa(args.steps)
         print(f"[bench] sliding-window attention step: {swa_res['ms_per_step']} ms",
               file=sys.stderr, flush=True)
-    extra = fwd16k = None
+    extra = fwd16k = tiles = None
     if not args.no_extras:
         extra = bench_cold_and_copy(step)
         print(f"[bench] cold step: {extra['cold_ms_per_step_median']} ms", file=sys.stderr,
@@ -883,6 +936,10 @@ def main():
         fwd16k = bench_train16k_fwd(args.steps, x_fwd)
         print(f"[bench] 16K forward (one group): {fwd16k['ms_per_step']} ms", file=sys.stderr,
               flush=True)
+        tiles = bench_tile_sizes(args.steps)
+        print("[bench] other tile sizes: " + ", ".join(f"{kk} {v['ms_per_step']} ms"
+                                                       for kk, v in tiles.items()),
+              file=sys.stderr, flush=True)
     gumbel = None
     if not args.no_gumbel:
         bufs = (idx, score, w, o, lse, dq, dk, dv, dw, dscore, dlq, dlk, wsr, wsb)
@@ -941,6 +998,7 @@ def main():
         "long_context": long_ctx or None,
         "cold_and_copy": extra,
         "train16k_fwd": fwd16k,
+        "tile_sizes": tiles,
         "gumbel_train_step": gumbel,
         "sliding_window_step": swa_res,
         "wall_s_timed": round(wall, 3),
