@@ -109,6 +109,8 @@ gca_status check_shape(const gca_shape* s, int op, Sizes* z) {
 #endif
 constexpr int64_t kScanTargetWgs = GCA_SCAN_TARGET_WGS;
 constexpr int64_t kMergeMax = 4096;  // partial keys per query the merge kernel holds in LDS
+constexpr int64_t kFewQueries = 4;   // query chunks per head up to which k_scan_few_bf16 runs
+constexpr int64_t kFewSlice = 256;   // its candidates per workgroup
 
 gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
   gca::ScanPlan p{};
@@ -134,6 +136,14 @@ gca::ScanPlan plan_scan(const gca_shape* s, const Sizes& z) {
   len = ((len + 127) / 128) * 128;
   p.split_len = len;
   p.nsplit = (int)((s->n_key + len - 1) / len);
+  // A few queries per head (decoding steps): slices of 256 candidates, one
+  // workgroup per (head, query, slice), while the merge can hold the lists.
+  const int64_t few_split = (s->n_key + kFewSlice - 1) / kFewSlice;
+  if (s->n_query <= kFewQueries && few_split * p.kmax <= kMergeMax) {
+    p.few = 1;
+    p.split_len = kFewSlice;
+    p.nsplit = (int)few_split;
+  }
   return p;
 }
 
@@ -272,7 +282,8 @@ static gca_status retrieve_impl(const char* fn, const gca_shape* shape, int nois
     if (!aligned(ws, kAlign)) return fail(GCA_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
   }
   const int64_t nblk = shape->dtype == GCA_BF16
-                           ? z.heads * plan.nsplit * (int64_t)plan.n_qtiles
+                           ? z.heads * plan.nsplit *
+                                 (plan.few ? shape->n_query : (int64_t)plan.n_qtiles)
                            : (z.q_rows + 63) / 64;
   if (nblk > 0x7fffffffLL) return fail(GCA_ERR_UNSUPPORTED, "retrieval grid too large");
   gca::LaunchRetrieve a{};

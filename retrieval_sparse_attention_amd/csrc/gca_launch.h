@@ -14,6 +14,8 @@ struct ScanPlan {
   int n_qtiles;      // ceil(n_query / 32)
   int nsplit;        // candidate slices per (head, query tile)
   int64_t split_len; // candidates per slice (multiple of 128)
+  int few;           // 1: one workgroup per (head, query, 256-candidate slice) in the
+                     // plain bf16 scan (k_scan_few_bf16); split_len is then 256
 };
 
 struct LaunchRetrieve {

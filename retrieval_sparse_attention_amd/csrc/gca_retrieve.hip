@@ -632,6 +632,95 @@ __global__ __launch_bounds__(256, 3) void k_scan_topk_bf16(
 }
 
 // ---------------------------------------------------------------------------
+// bf16 scan for a few queries per head (a decoding step scores one new chunk's
+// landmark against the whole context).  In k_scan_topk_bf16 such a query
+// would fill one column of a 32-query MFMA tile, and the tile's fixed costs
+// (bucket set-up, compactions over 32 queries) would set the step's latency.
+// Here one workgroup takes one (head, query) row and 256 consecutive
+// candidates, one landmark row per DL / 8 lanes (16 bytes each, so every wave
+// load covers whole rows), and writes the slice's KMAX best keys to the list
+// the merge kernel reads.  Grid: heads * n_query * nsplit, slice sp of row
+// (head, q) at block (head * n_query + q) * nsplit + sp.
+//   1. all of the slice's landmark loads are issued at once; each lane forms
+//      the float32 dot product of its 8 dimensions, and DPP moves sum the
+//      row's lanes (quad swaps, then the 8-lane mirror for DL = 64);
+//   2. key = (ordered score bits, ~j) as in the other scans, 0 for j past the
+//      query's candidates (j >= q_pos - 1 or >= n_key);
+//   3. each wave ranks its 64 keys among themselves in LDS; a key beaten by
+//      KMAX keys of its own wave cannot be among the slice's KMAX best, so at
+//      most 4 * KMAX survivors are ranked against each other, and rank r < KMAX
+//      goes to list entry r (entries past the slice's valid keys are 0).
+// ---------------------------------------------------------------------------
+template <int DL, int KMAX>
+__global__ __launch_bounds__(256) void k_scan_few_bf16(
+    const bf16* __restrict__ lq, const bf16* __restrict__ lk, const int32_t* __restrict__ q_pos,
+    int64_t n_query, int64_t n_key, int nsplit, float score_scale, uint64_t* __restrict__ part) {
+  constexpr int LPR = DL / 8;     // lanes per landmark row
+  constexpr int RPP = 256 / LPR;  // rows per pass of the workgroup
+  constexpr int NP = LPR;         // passes over the slice's 256 rows
+  static_assert(DL == 64 || DL == 32, "landmark rows of 64 or 32 bf16 values");
+  __shared__ __align__(16) uint64_t keys[256];
+  __shared__ __align__(16) uint64_t surv[4 * KMAX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sp = (int)(blockIdx.x % nsplit);
+  const int64_t qrow = blockIdx.x / nsplit;  // = head * n_query + q
+  const int64_t head = qrow / n_query;
+  const int64_t pos = q_pos[qrow - head * n_query];
+  int64_t n_cand = pos - 1 < n_key ? pos - 1 : n_key;
+  if (n_cand < 0) n_cand = 0;
+  const int64_t c0 = (int64_t)sp * 256;
+  const int p = tid % LPR, r0 = tid / LPR;  // dims 8p .. 8p+7 of row r0 of each pass
+  const bf16x8 qv = *(const bf16x8*)(lq + qrow * DL + 8 * p);
+  const bf16* lk_head = lk + head * n_key * DL;
+  bf16x8 kv[NP];
+#pragma unroll
+  for (int s = 0; s < NP; ++s) {
+    const int64_t j = c0 + s * RPP + r0;
+    kv[s] = *(const bf16x8*)(lk_head + (j < n_key ? j : n_key - 1) * DL + 8 * p);
+  }
+  if (tid < 4 * KMAX) surv[tid] = 0;
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] = (float)qv[e];
+#pragma unroll
+  for (int s = 0; s < NP; ++s) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(qf[e], (float)kv[s][e], acc);
+    acc += dpp_f<0xB1>(acc);                 // quad_perm [1,0,3,2]
+    acc += dpp_f<0x4E>(acc);                 // quad_perm [2,3,0,1]
+    if (LPR == 8) acc += dpp_f<0x141>(acc);  // row_half_mirror: the other 4 lanes
+    const int rl = s * RPP + r0;
+    const int64_t j = c0 + rl;
+    if (p == 0) keys[rl] = j < n_cand ? make_key(acc * score_scale + 0.0f, (int)j) : 0;
+  }
+  __syncthreads();
+  const uint64_t mine = keys[tid];
+  int rw = 0;  // keys of this wave above mine
+#pragma unroll 8
+  for (int u = 0; u < 64; u += 2) {
+    const ulonglong2 o = *(const ulonglong2*)&keys[64 * wave + u];
+    rw += (o.x > mine ? 1 : 0) + (o.y > mine ? 1 : 0);
+  }
+  const bool keep = mine != 0 && rw < KMAX;
+  const uint64_t mask = __ballot(keep);
+  if (keep)
+    surv[KMAX * wave + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] =
+        mine;
+  const int nv = __syncthreads_count(keep);
+  uint64_t* dst = part + (qrow * nsplit + sp) * KMAX;
+  if (tid < 4 * KMAX) {
+    const uint64_t me = surv[tid];
+    int r = 0;
+#pragma unroll
+    for (int u = 0; u < 4 * KMAX; ++u) r += surv[u] > me ? 1 : 0;
+    if (me != 0 && r < KMAX) dst[r] = me;
+  }
+  if (tid >= nv && tid < KMAX) dst[tid] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Merge of the per-slice lists: one wave per (head, query) row, n = nsplit *
 // KMAX keys (0 = empty).  The k-th largest of the 64 lane maxima bounds the
 // k-th best key from below; entries at or above it are packed into LDS and
@@ -813,7 +902,17 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
     const int64_t nblk = heads * pl.nsplit * pl.n_qtiles;
     {
     KernelTimer timer(kKernScan, a.stream);
-    if (a.dl == 64)
+    if (pl.few && !NOISE) {
+      const unsigned fblk = (unsigned)(heads * a.n_query * pl.nsplit);
+      if (a.dl == 64)
+        hipLaunchKernelGGL((k_scan_few_bf16<64, KMAX>), dim3(fblk), dim3(256), 0, a.stream,
+                           (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query, a.n_key,
+                           pl.nsplit, a.score_scale, a.part);
+      else
+        hipLaunchKernelGGL((k_scan_few_bf16<32, KMAX>), dim3(fblk), dim3(256), 0, a.stream,
+                           (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query, a.n_key,
+                           pl.nsplit, a.score_scale, a.part);
+    } else if (a.dl == 64)
       hipLaunchKernelGGL((k_scan_topk_bf16<64, KMAX, NOISE>), dim3((unsigned)nblk), dim3(256), 0,
                          a.stream, (const bf16*)a.lq, (const bf16*)a.lk, a.q_pos, a.n_query,
                          a.n_key, pl.n_qtiles, pl.nsplit, pl.split_len, a.score_scale, a.k,

@@ -167,6 +167,62 @@ def test_bf16_long_slices_mixed_positions(k, dl):
     close("w", f64(w), r_w, True, mask=sep)
 
 
+@pytest.mark.parametrize("nq,nk,k,dl,pos", [
+    (1, 1025, 8, 64, [1026]),                     # 5 slices, the last holds one candidate
+    (4, 5000, 8, 64, [0, 6, 257, 5001]),          # none, fewer than k, one slice + 1, all
+    (3, 20000, 16, 64, [1, 12801, 19999]),        # 79 slices, k = 16
+    (4, 65536, 16, 64, [513, 30000, 65536, 65537]),  # 256 slices x 16 = the merge's 4096
+    (2, 3000, 4, 32, [2000, 3001]),               # 32-dimensional landmarks
+    (4, 65537, 16, 64, [65538, 2, 40000, 257]),   # 257 slices would pass 4096: 32-query path
+], ids=["one_query", "edges", "k16", "merge_max", "dl32", "past_merge_max"])
+def test_bf16_few_query_scan(nq, nk, k, dl, pos):
+    """Retrieval for up to 4 query chunks per head (decoding steps) takes one
+    workgroup per (head, query, 256-candidate slice) before the merge; indices
+    bit-exact where the k-th score is separated, scores and weights within bf16
+    tolerance, on 12 heads."""
+    from oracle import condition
+    B, H = 2, 6
+    cfg = synth.workload("retrieve16m", B=B, H=H, n_query=nq, n_key=nk, k=k, Dl=dl)
+    rng = np.random.default_rng(nq * 1000 + k + dl)
+    lq = torch.from_numpy((rng.standard_normal((1, B, H, nq, dl)) / 8).astype(np.float32))
+    lk = torch.from_numpy((rng.standard_normal((1, B, H, nk, dl)) / 8).astype(np.float32))
+    lq, lk = lq.bfloat16(), lk.bfloat16()
+    q_pos = np.array(pos, np.int32)
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(lq), dev(lk), dev(torch.from_numpy(q_pos)))
+    lq64, lk64 = f64(lq), f64(lk)
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, q_pos, k, cfg["score_scale"],
+                                       cfg["softmax_one"])
+    n_cand = np.clip(q_pos.astype(np.int64) - 1, 0, nk)
+    sep = np.stack([condition.gap_ok(lq64[0, b, h], lk64[0, b, h], n_cand, k,
+                                     cfg["score_scale"], 1e-5)
+                    for b in range(B) for h in range(H)]).reshape(1, B, H, nq)
+    assert sep.mean() > 0.9
+    assert np.array_equal(idx.cpu().numpy()[sep], r_idx[sep])
+    close("score", f64(score), r_score, True, mask=sep)
+    close("w", f64(w), r_w, True, mask=sep)
+
+
+def test_bf16_few_query_scan_ties():
+    """Every landmark equal: all scores tie, so the k chunks of lowest index are
+    taken, in ascending order, with equal weights (score desc, index asc)."""
+    B, H, nq, nk, k = 1, 3, 2, 4000, 8
+    cfg = synth.workload("retrieve16m", B=B, H=H, n_query=nq, n_key=nk, k=k)
+    rng = np.random.default_rng(77)
+    row = torch.from_numpy((rng.standard_normal(64) / 8).astype(np.float32)).bfloat16()
+    lq = torch.from_numpy((rng.standard_normal((1, B, H, nq, 64)) / 8).astype(np.float32))
+    lq = lq.bfloat16()
+    lk = row.expand(1, B, H, nk, 64).contiguous()
+    q_pos = np.array([4001, 1500], np.int32)
+    idx, score, w = run_retrieve(shape_of(cfg), dev(lq), dev(lk), dev(torch.from_numpy(q_pos)))
+    r_idx, r_score, r_w = orc.retrieve(f64(lq), f64(lk), q_pos, k, cfg["score_scale"],
+                                       cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    assert (r_idx == np.arange(k)).all()
+    close("score", f64(score), r_score, True)
+    close("w", f64(w), r_w, True)
+
+
 def test_bf16_edge_positions():
     """q_pos giving 0, fewer than k, exactly k and all candidates; n_key not a multiple of 32."""
     cfg = synth.workload("train16k_fwdbwd_g2", G=1, B=1, H=2, n_query=6, n_key=45)
