@@ -173,8 +173,10 @@ def _ptr(t, name):
 
 
 def _stream():
+    # torch's current stream of the current device, as a raw HIP stream handle
+    # (the direct getter: a Stream object per call costs microseconds)
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
 
 
 def gca_workspace_size(shape, op):
