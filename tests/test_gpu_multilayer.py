@@ -80,8 +80,9 @@ def _oracle_group(cfg, base, layers, r_idx, r_w):
     ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72)),
     ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=72, n_key=72, D=32)),
     ("train16k_fwdbwd_g2", dict(B=1, H=2, n_query=40, n_key=40, S=16, D=32)),
+    ("train16k_fwdbwd_g2", dict(B=1, H=3, n_query=70, n_key=70, S=16, D=64)),
     ("tiny_fp32", dict(H=3)),
-], ids=["bf16", "bf16_d32", "bf16_s16_d32", "fp32"])
+], ids=["bf16", "bf16_d32", "bf16_s16_d32", "bf16_s16_d64", "fp32"])
 def test_one_retrieval_three_layers_accumulate(name, over):
     L = 3
     cfg, base, layers = _layers(name, L, **over)
