@@ -60,10 +60,24 @@ def test_full_train16k_forward():
 def test_full_train16k_fwdbwd_two_groups():
     """G=2 off-by-one training step at full size: every index, 3 sampled heads
     for all gradients, 64 sampled forward tiles."""
+    _full_train_step()
+
+
+@pytest.mark.parametrize("S,D", [(64, 32), (16, 64), (16, 32)],
+                         ids=["s64_d32", "s16_d64", "s16_d32"])
+def test_full_train16k_fwdbwd_other_tiles(S, D):
+    """The same 16K-token G=2 training step at the other MFMA tile sizes, as
+    bench.py times them (16384 / S chunks per head)."""
+    n = 16384 // S
+    _full_train_step(S=S, D=D, n_query=n, n_key=n)
+
+
+def _full_train_step(**over):
     name = "train16k_fwdbwd_g2"
-    cfg = synth.workload(name)
-    print(f"[full] {name}: generating inputs", flush=True)
-    x = synth.training_inputs(name, accept=accept_for(cfg))
+    cfg = synth.workload(name, **over)
+    n = cfg["n_query"]
+    print(f"[full] {name} {over}: generating inputs", flush=True)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
     shape = shape_of(cfg)
     d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
     idx, score, w = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
@@ -80,7 +94,7 @@ def test_full_train16k_fwdbwd_two_groups():
     rng = np.random.default_rng(22)
     qs = [(int(a), int(b), int(h), int(t)) for a, b, h, t in zip(
         rng.integers(0, 2, 64), rng.integers(0, 4, 64), rng.integers(0, 12, 64),
-        rng.integers(0, 256, 64))]
+        rng.integers(0, n, 64))]
     r_o, _ = orc.forward(q64, k64, v64, r_idx, r_w, cfg["attn_scale"], queries=qs)
     sel = tuple(np.array(qs).T)
     close("o", f64(o)[sel], r_o[sel], True)
