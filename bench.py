@@ -123,6 +123,60 @@ def roofline_entry(name, avg_s, work):
                 unit="GB/s", frac=round(ach / (HBM_PEAK / 1e9), 4))
 
 
+def measure_peaks(reps=10):
+    """Peaks of the GPU at hand, from the microbenchmarks built into the library
+    (include/gca_peaks.h): a streaming read of 2 GiB, a 1 GiB device copy and a loop
+    of independent 16x16x32 bf16 MFMAs; median of reps launches each (HIP events)."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    out = torch.empty(gca.PEAK_OUT_BYTES, dtype=torch.uint8, device="cuda")
+    n_read, n_copy = 2 << 30, 1 << 30
+    src = torch.ones(n_read, dtype=torch.uint8, device="cuda")
+    t_read = timed(lambda: gca.gca_peak_read(src, out))
+    dst = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
+    t_copy = timed(lambda: gca.gca_peak_copy(src[:n_copy], dst))
+    del src, dst
+    mf = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    flops = [0.0]
+
+    def mfma():
+        flops[0] = gca.gca_peak_mfma(mf, 2048)
+
+    t_mfma = timed(mfma)
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(n_read / t_read / 1e9, 1),
+            "copy_read_plus_write_GBps": round(2 * n_copy / t_copy / 1e9, 1),
+            "mfma_bf16_dense_TFLOPs": round(flops[0] / t_mfma / 1e12, 1),
+            "note": "gca_peak_read (2 GiB), gca_peak_copy (1 GiB), gca_peak_mfma (16x16x32 "
+                    "bf16, 4 waves per SIMD, 8 independent accumulators per wave)"}
+
+
+def with_measured(entry, peaks):
+    """Adds the fraction of the measured peak of the entry's bound to a roofline entry."""
+    if peaks is None:
+        return entry
+    mp = peaks["hbm_read_GBps"] if entry["bound"] == "hbm" else peaks["mfma_bf16_dense_TFLOPs"]
+    entry["measured_peak"] = mp
+    entry["frac_of_measured_peak"] = round(entry["achieved"] / mp, 4)
+    return entry
+
+
 def traffic_for(kernel, digest):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -889,7 +943,11 @@ def main():
             kernels[name] = dict(avg_us=round(tot / n * 1e3, 2), launches=n)
     dom = max(kernels,
               key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
-    roof = roofline_entry(dom, kernels[dom]["avg_us"] * 1e-6, work[dom])
+    peaks = measure_peaks()
+    print(f"[bench] measured peaks: {peaks['hbm_read_GBps']} GB/s read, "
+          f"{peaks['copy_read_plus_write_GBps']} GB/s copy, "
+          f"{peaks['mfma_bf16_dense_TFLOPs']} TFLOP/s bf16 MFMA", file=sys.stderr, flush=True)
+    roof = with_measured(roofline_entry(dom, kernels[dom]["avg_us"] * 1e-6, work[dom]), peaks)
     sw = step_work(cfg, pairs)
     t_step_roof = max(sw["bytes"] / HBM_PEAK, sw["flops"] / MFMA_BF16_PEAK)
     step_roof = {"bytes": sw["bytes"], "flops": sw["flops"],
@@ -898,6 +956,10 @@ def main():
                  "roofline_us": round(t_step_roof * 1e6, 2),
                  "roofline_tokens_per_s": round(B * Nq * S / t_step_roof, 1),
                  "frac": round(t_step_roof / (step_ms * 1e-3), 4),
+                 "frac_of_measured_peaks": round(
+                     max(sw["bytes"] / (peaks["hbm_read_GBps"] * 1e9),
+                         sw["flops"] / (peaks["mfma_bf16_dense_TFLOPs"] * 1e12))
+                     / (step_ms * 1e-3), 4),
                  "note": "whole step (retrieve + forward + backward) against max(HBM, MFMA) "
                          "time of its algorithmic bytes and flops (5 tile products per pair "
                          "in the backward, as the math needs)"}
@@ -907,8 +969,10 @@ def main():
     roof["algorithmic_flops"] = work[dom]["flops"]
     for name in kernels:
         if name in work:
-            e = roofline_entry(name, kernels[name]["avg_us"] * 1e-6, work[name])
-            kernels[name].update(bound=e["bound"], frac=e["frac"])
+            e = with_measured(roofline_entry(name, kernels[name]["avg_us"] * 1e-6, work[name]),
+                              peaks)
+            kernels[name].update(bound=e["bound"], frac=e["frac"],
+                                 frac_of_measured_peak=e["frac_of_measured_peak"])
     print(f"[bench] timed {args.steps} steps: {step_ms:.3f} ms/step, dominant {dom}",
           file=sys.stderr, flush=True)
     if args.copy_ref > 0:
@@ -948,6 +1012,10 @@ def main():
     long_ctx = {}
     if not args.no_long_context:
         long_ctx["retrieve16m"] = bench_retrieve16m(inp=inp16m)
+        r16 = long_ctx["retrieve16m"]
+        if r16.get("landmark_scan_GBps"):
+            r16["landmark_scan_frac_of_measured_read"] = round(
+                r16["landmark_scan_GBps"] / peaks["hbm_read_GBps"], 4)
         print(f"[bench] 16M retrieval: {long_ctx['retrieve16m']['retrieve_fwd_latency_ms']} ms",
               file=sys.stderr, flush=True)
         long_ctx["infer1m_step"] = bench_infer1m(args.infer_steps, inp1m)
@@ -990,6 +1058,7 @@ def main():
                    "step": "gca_retrieve + gca_forward + gca_backward"},
         "roofline": roof,
         "step_roofline": step_roof,
+        "measured_peaks": peaks,
         "ms_per_step_with_kernel_events": round(step_ms_timed, 4),
         "cpu_baseline": cpu,
         "kernels": kernels,

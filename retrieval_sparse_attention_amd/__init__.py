@@ -46,6 +46,9 @@ EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_works
             "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
             "gca_swa_forward", "gca_swa_backward")
+# include/gca_peaks.h: microbenchmarks for the peaks measured on the GPU at hand
+PEAK_EXPORTED = ("gca_peak_read", "gca_peak_copy", "gca_peak_mfma")
+PEAK_OUT_BYTES = 2048 * 256 * 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -132,6 +135,12 @@ def load():
     lib.gca_swa_backward.restype = ctypes.c_int
     lib.gca_swa_backward.argtypes = [swp] + [vp] * 10 + [sz, vp]
     lib.gca_num_kernels.restype = ctypes.c_int
+    lib.gca_peak_read.argtypes = [vp, sz, vp, vp]
+    lib.gca_peak_read.restype = ctypes.c_int
+    lib.gca_peak_copy.argtypes = [vp, vp, sz, vp]
+    lib.gca_peak_copy.restype = ctypes.c_int
+    lib.gca_peak_mfma.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double), vp]
+    lib.gca_peak_mfma.restype = ctypes.c_int
     lib.gca_num_kernels.argtypes = []
     lib.gca_kernel_name.restype = ctypes.c_char_p
     lib.gca_kernel_name.argtypes = [ctypes.c_int]
@@ -313,3 +322,22 @@ def gca_timing_collect():
     cnt = (ctypes.c_int64 * n)()
     _check(load().gca_timing_collect(ms, cnt))
     return {gca_kernel_name(i): (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+def gca_peak_read(src, out):
+    """Streaming read of the device tensor src (its bytes); out: >= PEAK_OUT_BYTES."""
+    _check(load().gca_peak_read(_ptr(src, "src"), ctypes.c_size_t(src.numel() * src.element_size()),
+                                _ptr(out, "out"), _stream()))
+
+
+def gca_peak_copy(src, dst):
+    """Streaming copy of src's bytes into dst (same size, device tensors)."""
+    _check(load().gca_peak_copy(_ptr(src, "src"), _ptr(dst, "dst"),
+                                ctypes.c_size_t(src.numel() * src.element_size()), _stream()))
+
+
+def gca_peak_mfma(out, iters):
+    """Loop of independent 16x16x32 bf16 MFMAs; returns the launch's flop count."""
+    flops = ctypes.c_double(0.0)
+    _check(load().gca_peak_mfma(_ptr(out, "out"), int(iters), ctypes.byref(flops), _stream()))
+    return flops.value

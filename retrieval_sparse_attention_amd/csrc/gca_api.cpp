@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "gca.h"
+#include "gca_peaks.h"
 #include "gca_launch.h"
 
 namespace {
@@ -630,6 +631,41 @@ gca_status gca_backward_accumulate(const gca_shape* shape, const void* q, const 
   return backward_impl("gca_backward_accumulate", 1, shape, q, k, v, idx, w, lse, dout, lq, lk,
                        dq, dk_acc, dv_acc, dw_acc, dscore_acc, dlq_acc, dlk_acc, ws, ws_bytes,
                        stream);
+}
+
+}  // extern "C"
+
+// Microbenchmarks for the measured peaks (gca_peaks.h).
+extern "C" {
+
+gca_status gca_peak_read(const void* src, size_t bytes, void* out, void* stream) {
+  GCA_TRY(need(src, "src", 16));
+  GCA_TRY(need(out, "out", 4));
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "gca_peak_read: bytes must be a positive multiple of 16");
+  hipStream_t st = (hipStream_t)stream;
+  return device_status(gca::launch_peak_read(src, bytes, out, st), st, "gca_peak_read");
+}
+
+gca_status gca_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  GCA_TRY(need(src, "src", 16));
+  GCA_TRY(need(dst, "dst", 16));
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "gca_peak_copy: bytes must be a positive multiple of 16");
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "gca_peak_copy: src and dst overlap");
+  hipStream_t st = (hipStream_t)stream;
+  return device_status(gca::launch_peak_copy(src, dst, bytes, st), st, "gca_peak_copy");
+}
+
+gca_status gca_peak_mfma(void* out, int iters, double* flops, void* stream) {
+  GCA_TRY(need(out, "out", 4));
+  if (iters < 1 || iters > (1 << 20))
+    return fail(GCA_ERR_INVALID_ARGUMENT, "gca_peak_mfma: iters must be in 1 .. 2^20");
+  if (flops) *flops = 1024.0 * 4.0 * (double)iters * 8.0 * (16.0 * 16.0 * 32.0 * 2.0);
+  hipStream_t st = (hipStream_t)stream;
+  return device_status(gca::launch_peak_mfma(out, iters, st), st, "gca_peak_mfma");
 }
 
 }  // extern "C"

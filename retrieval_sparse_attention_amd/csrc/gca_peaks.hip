@@ -1,0 +1,104 @@
+// Microbenchmarks for the peaks measured on the GPU at hand (include/gca_peaks.h):
+// a streaming read, a streaming copy and a loop of independent 16x16x32 bf16
+// MFMAs.  Grids are fixed: 2048 workgroups of 256 threads for the memory
+// kernels (eight per CU on 256 CUs), 1024 for the MFMA loop (four waves per
+// SIMD).  They share no arithmetic with the GCA kernels.
+
+#include "gca_device.h"
+#include "gca_launch.h"
+
+namespace gca {
+
+constexpr int kPeakMemBlocks = 2048;
+constexpr int kPeakMfmaBlocks = 1024;
+
+// Each workgroup streams one contiguous range (whole DRAM pages, one open
+// stream per workgroup); every thread keeps kPeakU 16-byte loads in flight and
+// folds all four words of each into one 32-bit value, stored at the end.  The
+// read uses nontemporal loads (data read once need not stay in the caches):
+// 6.6-6.7 TB/s against 5.9-6.2 with plain loads on one box.
+constexpr int kPeakU = 8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ src, int64_t n,
+                                                   uint32_t* __restrict__ out) {
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = beg + per < n ? beg + per : n;
+  uint32_t acc = 0;
+  int64_t i = beg + threadIdx.x;
+  for (; i + (kPeakU - 1) * 256 < end; i += kPeakU * 256) {
+    uint4 v[kPeakU];
+#pragma unroll
+    for (int u = 0; u < kPeakU; ++u) {
+      const u32x4 t = __builtin_nontemporal_load((const u32x4*)(src + i + u * 256));
+      v[u] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < kPeakU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < end; i += 256) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_peak_copy(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst, int64_t n) {
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = beg + per < n ? beg + per : n;
+  int64_t i = beg + threadIdx.x;
+  for (; i + (kPeakU - 1) * 256 < end; i += kPeakU * 256) {
+    uint4 v[kPeakU];
+#pragma unroll
+    for (int u = 0; u < kPeakU; ++u) v[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < kPeakU; ++u) dst[i + u * 256] = v[u];
+  }
+  for (; i < end; i += 256) dst[i] = src[i];
+}
+
+// Eight accumulators per wave, each updated once per round: consecutive MFMAs
+// never depend on each other, so the matrix pipe issues back to back.
+__global__ __launch_bounds__(256) void k_peak_mfma(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (bf16)(0.001f * (float)(lane + e));
+    b[e] = (bf16)(0.002f * (float)(lane - e));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = zero4();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = mfma16x16x32(a, b, acc[r]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) s += (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+hipError_t launch_peak_read(const void* src, size_t bytes, void* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_peak_read, dim3(kPeakMemBlocks), dim3(256), 0, stream, (const uint4*)src,
+                     (int64_t)(bytes / 16), (uint32_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(k_peak_copy, dim3(kPeakMemBlocks), dim3(256), 0, stream, (const uint4*)src,
+                     (uint4*)dst, (int64_t)(bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_mfma(void* out, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(k_peak_mfma, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, (float*)out,
+                     iters);
+  return hipGetLastError();
+}
+
+}  // namespace gca

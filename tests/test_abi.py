@@ -10,11 +10,12 @@ import pytest
 import retrieval_sparse_attention_amd as gca
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gca.h")
+PEAKS_HEADER = os.path.join(os.path.dirname(HEADER), "gca_peaks.h")
 P = ctypes.c_void_p
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=None):
+    text = open(header or HEADER).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gca_\w+)\s*\(", text, re.M)))
 
 
@@ -24,6 +25,24 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(gca.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
+    peaks = _declared(PEAKS_HEADER)
+    assert set(peaks) == set(gca.PEAK_EXPORTED)
+    for n in peaks:
+        assert hasattr(lib, n), n
+
+
+def test_peak_calls_reject_bad_arguments():
+    # validated on the host before any launch (fake device addresses are never touched)
+    st, msg = _status("gca_peak_read", None, ctypes.c_size_t(16), A, None)
+    assert st == 1 and "src is NULL" in msg
+    st, msg = _status("gca_peak_read", A, ctypes.c_size_t(24), A, None)
+    assert st == 1 and "multiple of 16" in msg
+    st, msg = _status("gca_peak_copy", A, A, ctypes.c_size_t(64), None)
+    assert st == 1 and "overlap" in msg
+    st, msg = _status("gca_peak_mfma", A, 0, None, None)
+    assert st == 1 and "iters" in msg
+    assert "2048 * 256 * 4" in open(PEAKS_HEADER).read()
+    assert gca.PEAK_OUT_BYTES == 2048 * 256 * 4
 
 
 def test_version_and_strings():
