@@ -72,6 +72,31 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t nblk) {
   return (bid % 8) * (nblk / 8) + bid / 8;
 }
 
+// Order in which key chunks go out.  Each XCD works through one contiguous
+// range of tiles (xcd_tile), head after head, so that the Q/dO tiles in use
+// are those of about one head, which its L2 can nearly hold.  A chunk's work
+// grows with its reverse list, and in causal training the early chunks
+// collect the longest lists (about k ln(n/c) entries for chunk c): in plain
+// head order the range's last heads would start theirs near the end of the
+// grid and run alone.  So the first 32 chunks of the range's last head and
+// the first 8 of the head before it go out first; the rest keep head order.
+__device__ __forceinline__ int64_t kv_tile_order(int64_t i, int64_t n_key, int64_t nblk) {
+  if (nblk % 8 != 0) return i;  // xcd_tile is the identity then
+  const int64_t R = nblk / 8;
+  const int64_t s0 = (i / R) * R, li = i - s0;  // this XCD's range [s0, s0 + R)
+  const int64_t hl = (s0 + R - 1) / n_key;      // its last head
+  const int64_t b1 = hl * n_key, b2 = (hl - 1) * n_key;
+  int64_t f1 = n_key < 32 ? n_key : 32, f2 = n_key < 8 ? n_key : 8;
+  if (b1 < s0 || b1 + f1 > s0 + R) f1 = 0;  // hoisted blocks lie inside the range
+  if (hl < 1 || b2 < s0) f2 = 0;
+  if (li < f1) return b1 + li;
+  if (li < f1 + f2) return b2 + (li - f1);
+  int64_t t = s0 + (li - f1 - f2);  // the rest in order, skipping both blocks
+  if (f2 && t >= b2) t += f2;
+  if (f1 && t >= b1) t += f1;
+  return t;
+}
+
 // Candidate order used by the top-k: higher score first, then lower chunk index.
 __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
