@@ -102,6 +102,9 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s16(
   const bf16* k_head = kk + head * n_key * TE;
   const bf16* v_head = v + head * n_key * TE;
   const float c2 = attn_scale * kLog2e;
+  float lsev[4];  // L rows of slots 4j + grp (topk <= 16)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lsev[j] = 0.0f;
   if (n > 0) {
     const int64_t c = uniform(s_c[wave][0]);
     dma.copy_async(tiles_lds[wave][0][0], k_head + c * TE);
@@ -137,8 +140,17 @@ __global__ __launch_bounds__(256) void k_fwd_bf16_s16(
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(ps, pv[e], oacc[dt][e]);
     }
-    if (lse_tile && grp == 0)
-      lse_tile[uniform(s_slot[wave][u]) * 16 + col] = attn_scale * m + fast_ln(l);
+    // this slot's L row, kept by the lanes with grp == u % 4 (every lane of a
+    // column holds m and l): a store here would be waited on by the next
+    // slot's copy wait
+    const float lv = attn_scale * m + fast_ln(l);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lsev[j] = (u == 4 * j + grp) ? lv : lsev[j];
+  }
+  if (lse_tile) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * j + grp < n) lse_tile[s_slot[wave][4 * j + grp] * 16 + col] = lsev[j];
   }
   // O[x][d]: this lane holds d = 16dt + 4g + 0..3 of row x = col
   bf16* orow = o + tile * TE + col * D + 4 * grp;
@@ -208,6 +220,9 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16_s16(
   const float* lse_tile = lse + tile * topk * 16;
   const float c2 = attn_scale * kLog2e;
   float l_next = 0.0f;
+  float dlt[4];  // D rows of valid slots 4j + grp (topk <= 16)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dlt[j] = 0.0f;
   if (n > 0) {
     const int i = uniform(s_list[wave][0]);
     const int64_t c = __builtin_amdgcn_readlane(c_lane, i);
@@ -248,7 +263,10 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16_s16(
     // D = rowsum(P dP~) = rowsum(P_w dP~) / w  (0 when w = 0)
     const float dsw = xor32_sum(xor16_sum(dp));
     const float dsum = wi > 0.0f ? dsw * fast_rcp(wi) : 0.0f;
-    if (grp == 0) delta_tile[i * 16 + col] = dsum;
+    // kept by the lanes with grp == u % 4 and stored after the loop (a store
+    // here would be waited on by the next slot's copy wait)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dlt[j] = (u == 4 * j + grp) ? dsum : dlt[j];
     const float part = row16_sum(dsum);  // over the 16 query rows
     if (lane == 0) s_dw[wave][i] = part;
     bf16x4 bs;
@@ -257,6 +275,9 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16_s16(
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) dqacc[dt] = mfma16x16x16(ka[dt], bs, dqacc[dt]);
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * j + grp < n) delta_tile[s_list[wave][4 * j + grp] * 16 + col] = dlt[j];
   bf16* dqrow = dq + tile * TE + col * D + 4 * grp;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
