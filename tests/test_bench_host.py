@@ -50,3 +50,14 @@ def test_training_step_work_model():
         rec = json.load(f)
     for name in ("scan_topk", "forward", "reverse_index", "backward_q", "backward_kv"):
         assert rec[f"{name}@train16k_fwdbwd_g2"]["algorithmic_bytes"] == work[name]["bytes"]
+
+
+def test_fraction_of_measured_peak():
+    """A roofline entry gains its achieved rate over the measured peak of its own bound."""
+    peaks = {"hbm_read_GBps": 6000.0, "mfma_bf16_dense_TFLOPs": 2000.0}
+    hbm = bench.with_measured(dict(bound="hbm", achieved=3000.0), peaks)
+    assert hbm["measured_peak"] == 6000.0 and hbm["frac_of_measured_peak"] == 0.5
+    mf = bench.with_measured(dict(bound="mfma", achieved=500.0), peaks)
+    assert mf["measured_peak"] == 2000.0 and mf["frac_of_measured_peak"] == 0.25
+    assert bench.with_measured(dict(bound="hbm", achieved=1.0), None) == dict(bound="hbm",
+                                                                            achieved=1.0)
