@@ -1,0 +1,101 @@
+"""Seeded random shapes through the whole path (retrieve -> forward ->
+backward, plus the accumulate mode) against the float64 oracle.
+
+Each case draws G, B, H, the chunk count, the chunk size and head_dim (the
+MFMA sizes 16/64 x 32/64 and odd VALU-path sizes), k from 1 to 16, the
+landmark width, the fusion-weight variant and bf16 or float32 elements, so
+that the library's dispatch between kernels (64- or 16-token MFMA tiles,
+half-width rows, the generic path; the scans by candidate count) is crossed
+with ragged grids and partial workgroups (float32 cases at the tiny
+workload's sizes, where its 1e-5 bound applies).  Definitions: long-context-modeling
+README, "Model Architecture" (per-chunk attention and fusion); paperhub.cn,
+authors' reply "Cmt 1" (Eq. 1 scores); paperlayer.ai summary, appendix B
+(the backward's gradients).  Tolerances as everywhere: float32 1e-5 max-abs;
+bf16 2e-2 max-abs and 1e-2 mean-relative; indices bit-exact (inputs drawn with
+a 1e-3 gap at the k-th score).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import retrieval_sparse_attention_amd as gca
+import synth
+from oracle import gca_oracle as orc
+from gpu_common import (accept_for, close, compare_lse, dev, f64, require_gpu, run_backward,
+                        run_forward, run_retrieve, shape_of)
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    bf = seed % 4 != 3  # every fourth case in float32
+    S, D = [(64, 64), (64, 32), (16, 64), (16, 32), (5, 7), (33, 20)][rng.integers(0, 6)]
+    n = int(rng.integers(1, 90))
+    over = dict(G=int(rng.integers(1, 3)), B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                n_query=n, n_key=n, S=S, D=D, k=int(rng.integers(1, 17)),
+                Dl=int((32, 64)[rng.integers(0, 2)]), softmax_one=int(rng.integers(0, 2)))
+    name = "train16k_fwdbwd_g2" if bf else "tiny_fp32"
+    if not bf:
+        # float32 cases stay at the tiny workload's sizes (S <= 16, D <= 32 with N(0, 1)
+        # values), where the 1e-5 max-abs bound is meant: at S = D = 64 the gradients'
+        # magnitudes reach ~50 and float32 rounding alone is of that order
+        over["S"], over["D"] = [(16, 32), (5, 7), (9, 13)][rng.integers(0, 3)]
+        over["Dl"] = int(rng.integers(1, 100))
+    return name, over
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_shape_full_path(seed):
+    name, over = _draw(seed)
+    print(f"[random] seed {seed}: {name} {over}", flush=True)
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
+    bf = cfg["dtype"] == "bf16"
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    idx, score, w = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
+    lq64, lk64 = f64(x["lq"]), f64(x["lk"])
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, x["q_pos"].numpy(), cfg["k"],
+                                       cfg["score_scale"], cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx), "top-k indices differ"
+    close("score", f64(score), r_score, bf)
+    close("w", f64(w), r_w, bf)
+    o, lse = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
+    q64, k64, v64, do64 = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"])
+    r_o, r_lse = orc.forward(q64, k64, v64, r_idx, r_w, cfg["attn_scale"])
+    close("o", f64(o), r_o, bf)
+    compare_lse(lse, r_lse, bf)
+    g = run_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"])
+    r = orc.backward(q64, k64, v64, r_idx, r_w, do64, lq64, lk64, cfg["attn_scale"],
+                     cfg["score_scale"])
+    for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+        close(key, f64(g[key]), r[key], bf)
+    # the accumulate mode on the same inputs, added to zeroed float32 buffers, gives
+    # the same gradients (dK, dV, dlk, dlq, dw, dscore accumulated, dQ written)
+    ws = torch.empty(gca.gca_workspace_size(shape, gca.OP_BACKWARD), dtype=torch.uint8,
+                     device="cuda")
+    acc = dict(dq=torch.empty_like(d["q"]),
+               dk=torch.zeros(tuple(d["k"].shape), dtype=torch.float32, device="cuda"),
+               dv=torch.zeros(tuple(d["v"].shape), dtype=torch.float32, device="cuda"),
+               dw=torch.zeros(tuple(w.shape), device="cuda"),
+               dscore=torch.zeros(tuple(w.shape), device="cuda"),
+               dlq=torch.zeros(tuple(d["lq"].shape), device="cuda"),
+               dlk=torch.zeros(tuple(d["lk"].shape), device="cuda"))
+    gca.gca_backward_accumulate(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"],
+                                d["lk"], acc["dq"], acc["dk"], acc["dv"], acc["dw"],
+                                acc["dscore"], acc["dlq"], acc["dlk"], ws=ws)
+    torch.cuda.synchronize()
+    close("dq (accumulate)", f64(acc["dq"]), r["dq"], bf)
+    for key in ("dk", "dv"):
+        close(f"{key} (accumulate)", f64(acc[key]), r[key], bf)
+    for key in ("dw", "dscore", "dlq", "dlk"):
+        close(f"{key} (accumulate)", f64(acc[key]), r[key], bf)
