@@ -99,3 +99,38 @@ def test_random_shape_full_path(seed):
         close(f"{key} (accumulate)", f64(acc[key]), r[key], bf)
     for key in ("dw", "dscore", "dlq", "dlk"):
         close(f"{key} (accumulate)", f64(acc[key]), r[key], bf)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_retrieval_shape(seed):
+    """Retrieval alone over long candidate lists: n_key 1025 .. 70000 and 1 .. 40 query
+    chunks per head, so that the scan's plan (few-query slices, 32-query tiles, the
+    merge's register or streamed widths) varies; indices bit-exact where the k-th
+    score is separated by 1e-5, scores and weights within bf16 tolerance."""
+    from oracle import condition
+    rng = np.random.default_rng(2000 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    nq = int((1, 2, 3, 4, 5, 17, 33, 40)[rng.integers(0, 8)])
+    nk = int(rng.integers(1025, 70000))
+    k = int(rng.integers(1, 17))
+    dl = int((32, 64)[rng.integers(0, 2)])
+    print(f"[random retrieval] seed {seed}: B={B} H={H} nq={nq} nk={nk} k={k} dl={dl}",
+          flush=True)
+    cfg = synth.workload("retrieve16m", B=B, H=H, n_query=nq, n_key=nk, k=k, Dl=dl)
+    lq = torch.from_numpy((rng.standard_normal((1, B, H, nq, dl)) / 8).astype(np.float32))
+    lk = torch.from_numpy((rng.standard_normal((1, B, H, nk, dl)) / 8).astype(np.float32))
+    lq, lk = lq.bfloat16(), lk.bfloat16()
+    q_pos = rng.integers(0, nk + 2, size=nq).astype(np.int32)
+    shape = shape_of(cfg)
+    idx, score, w = run_retrieve(shape, dev(lq), dev(lk), dev(torch.from_numpy(q_pos)))
+    lq64, lk64 = f64(lq), f64(lk)
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, q_pos, k, cfg["score_scale"],
+                                       cfg["softmax_one"])
+    n_cand = np.clip(q_pos.astype(np.int64) - 1, 0, nk)
+    sep = np.stack([condition.gap_ok(lq64[0, b, h], lk64[0, b, h], n_cand, k,
+                                     cfg["score_scale"], 1e-5)
+                    for b in range(B) for h in range(H)]).reshape(1, B, H, nq)
+    assert sep.mean() > 0.9
+    assert np.array_equal(idx.cpu().numpy()[sep], r_idx[sep])
+    close("score", f64(score), r_score, True, mask=sep)
+    close("w", f64(w), r_w, True, mask=sep)
