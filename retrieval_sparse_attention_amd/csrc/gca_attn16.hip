@@ -288,14 +288,9 @@ __global__ __launch_bounds__(256) void k_bwd_q_bf16_s16(
   }
   // dscore_i = w_i (dw_i - sum_l w_l dw_l) over the valid slots; lane i holds slot i
   __builtin_amdgcn_wave_barrier();
-  const float dw_lane = ok ? s_dw[wave][lane < 16 ? lane : 0] : 0.0f;
-  const float sw = wave_sum(ok ? w_lane * dw_lane : 0.0f);
-  const float ds_lane = ok ? w_lane * (dw_lane - sw) : 0.0f;
-  if (lane < topk) {
-    put<ACC>(dw_out + tile * topk + lane, dw_lane);
-    put<ACC>(dscore_out + tile * topk + lane, ds_lane);
-    if (ACC) ds_layer[tile * topk + lane] = ds_lane;  // this layer's dscore, for the key side
-  }
+  const float ds_lane = slot_dscore<ACC>(lane, topk, ok, w_lane, s_dw[wave][lane < 16 ? lane : 0],
+                                         dw_out + tile * topk, dscore_out + tile * topk,
+                                         ACC ? ds_layer + tile * topk : nullptr);
   if (dlq) {
     const bf16* lk_head = lk ? lk + head * n_key * dl : nullptr;
     for (int d = lane; d < dl; d += 64) {

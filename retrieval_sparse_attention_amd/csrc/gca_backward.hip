@@ -151,36 +151,27 @@ __global__ __launch_bounds__(512) void k_reverse_index(const int32_t* __restrict
   if (tid == 0) off[n_key] = base;
 }
 
-// Score / landmark epilogue of one query chunk, run by the whole workgroup.
-// dw_slot[i] holds dw_i (only valid slots); writes dw, dscore and dlq (ACC:
-// adds them to the float32 accumulators instead).  With no resident chunk
-// (lk_head null) every slot is empty and dlq is 0.
-
+// Score / landmark epilogue of one query chunk, run by a one-wave workgroup
+// (lane = thread).  dw_slot[i] holds dw_i (only valid slots); writes dw,
+// dscore and dlq (ACC: adds them to the float32 accumulators instead).  With
+// no resident chunk (lk_head null) every slot is empty and dlq is 0.
 template <typename LT, bool ACC>
-__device__ void score_epilogue(int tid, int nthreads, int topk, const int* slot_c,
-                               const float* wv, float* dw_slot, float* ds_slot,
-                               float* __restrict__ dw_out, float* __restrict__ dscore_out,
-                               float* __restrict__ ds_layer,
+__device__ void score_epilogue(int lane, int topk, const int* slot_c, const float* wv,
+                               const float* dw_slot, float* ds_slot, float* __restrict__ dw_out,
+                               float* __restrict__ dscore_out, float* __restrict__ ds_layer,
                                const LT* __restrict__ lk_head, float* __restrict__ dlq_row,
                                int dl, float score_scale) {
-  if (tid == 0) {
-    float sw = 0.0f;
-    for (int i = 0; i < topk; ++i)
-      if (slot_c[i] >= 0) sw += wv[i] * dw_slot[i];
-    for (int i = 0; i < topk; ++i) {
-      const bool ok = slot_c[i] >= 0;
-      ds_slot[i] = ok ? wv[i] * (dw_slot[i] - sw) : 0.0f;
-      put<ACC>(dw_out + i, ok ? dw_slot[i] : 0.0f);
-      put<ACC>(dscore_out + i, ds_slot[i]);
-      if (ACC) ds_layer[i] = ds_slot[i];  // this layer's dscore, for the key side
-    }
-  }
+  const int i = lane < topk ? lane : 0;
+  const bool ok = lane < topk && slot_c[i] >= 0;
+  const float ds = slot_dscore<ACC>(lane, topk, ok, wv[i], dw_slot[i], dw_out, dscore_out,
+                                    ds_layer);
+  if (lane < topk) ds_slot[lane] = ds;
   __syncthreads();
   if (dlq_row && !lk_head) {
     if (!ACC)
-      for (int d = tid; d < dl; d += nthreads) dlq_row[d] = 0.0f;
+      for (int d = lane; d < dl; d += 64) dlq_row[d] = 0.0f;
   } else if (dlq_row) {
-    for (int d = tid; d < dl; d += nthreads) {
+    for (int d = lane; d < dl; d += 64) {
       float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -310,7 +301,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   __shared__ float dw_part[4][16];
   __shared__ int slot_c[16];
   __shared__ float slot_w[16];
-  __shared__ float dw_slot[16];
   __shared__ float ds_slot[16];
   __shared__ int s_list[16];
   __shared__ int s_n;
@@ -318,6 +308,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   // D rows of the k slots, staged here and stored once at the end: a store per
   // slot would be waited on by the next slot's copy wait.
   __shared__ float s_delta[16 * 64];
+  // landmark rows lk[c_i] of the k slots for dlq, copied in with slot 0's tiles
+  __shared__ __align__(16) bf16 lk_lds[16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -378,6 +370,13 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   float l2_next = 0.0f;
   if (n > 0) {
     bwdq_issue(cx, 0, k_lds[0], v_lds[0]);
+    if (dlq && lk && wave < dl / 32) {
+      // 16-byte piece e of the 16 x dl row block: row e / (dl / 8); rows of empty
+      // slots and past topk take chunk 0 (their dscore is 0 or they are not read)
+      const int e = wave * 64 + lane, r = e / (dl / 8);
+      const int c = r < topk && slot_c[r] >= 0 ? slot_c[r] : 0;
+      copy16_async(lk_lds + wave * 512, lk + (head * n_key + c) * dl + (e % (dl / 8)) * 8);
+    }
     l2_next = cx.lse_row[uniform(s_list[0]) * 64];
   }
   for (int u = 0; u < n; u += 2) {
@@ -385,7 +384,11 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
     if (u + 1 < n)
       bwdq_slot(cx, u + 1, l2_next, bq, bdo, dqacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
   }
-  bf16* dqrow = dq + tile * (64 * D) + x * D + 4 * grp;
+  // the row offset is formed again here from an opaque copy of the thread
+  // index, so the compiler does not keep it live across the slot loop
+  int t2 = tid;
+  asm volatile("" : "+v"(t2));
+  bf16* dqrow = dq + tile * (64 * D) + (16 * (t2 >> 6) + (t2 & 15)) * D + 4 * ((t2 & 63) >> 4);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
     bf16x4 val;
@@ -395,12 +398,23 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   }
   __syncthreads();
   for (int e = tid; e < topk * 64; e += 256) delta[tile * topk * 64 + e] = s_delta[e];
-  if (tid < topk) dw_slot[tid] = (dw_part[0][tid] + dw_part[1][tid]) + (dw_part[2][tid] + dw_part[3][tid]);
+  if (wave == 0) {  // lane i: slot i
+    const int i = lane < topk ? lane : 0;
+    const float dwi = (dw_part[0][i] + dw_part[1][i]) + (dw_part[2][i] + dw_part[3][i]);
+    const float ds = slot_dscore<ACC>(lane, topk, lane < topk && slot_c[i] >= 0, slot_w[i], dwi,
+                                      dw_out + tile * topk, dscore_out + tile * topk,
+                                      ACC ? ds_layer + tile * topk : nullptr);
+    if (lane < topk) ds_slot[lane] = ds;
+  }
   __syncthreads();
-  score_epilogue<bf16, ACC>(tid, 256, topk, slot_c, slot_w, dw_slot, ds_slot,
-                            dw_out + tile * topk, dscore_out + tile * topk,
-                            ACC ? ds_layer + tile * topk : nullptr, lk ? lk + head * n_key * dl : nullptr,
-                       dlq ? dlq + tile * dl : nullptr, dl, score_scale);
+  // dlq = score_scale sum_i dscore_i lk[c_i] from the staged rows (0 with no
+  // valid slot; ACC then adds nothing where lk is absent)
+  if (dlq && tid < dl) {
+    float acc = 0.0f;
+    if (lk && s_n > 0)
+      for (int i = 0; i < topk; ++i) acc = fmaf(ds_slot[i], (float)lk_lds[i * dl + tid], acc);
+    if (lk || !ACC) put<ACC>(dlq + tile * dl + tid, score_scale * acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -736,7 +750,7 @@ __global__ __launch_bounds__(64) void k_bwd_q_gen(
       if (d < D) store_f(dqrow + d, dqa[d]);
   }
   __syncthreads();
-  score_epilogue<T, ACC>(x, 64, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
+  score_epilogue<T, ACC>(x, topk, slot_c, slot_w, dw_slot, ds_slot, dw_out + tile * topk,
                          dscore_out + tile * topk, ACC ? ds_layer + tile * topk : nullptr,
                          lk ? lk + head * n_key * dl : nullptr, dlq ? dlq + tile * dl : nullptr,
                          dl, score_scale);

@@ -264,6 +264,25 @@ struct TileDma {
   }
 };
 
+// Asynchronous copy of 16 bytes per lane from a per-lane global address `src`
+// to LDS at lds_block + 16 * lane (the wave's 1 KB block; lds_block must be
+// wave-uniform), issued like TileDma::copy_async: the compiler does not track
+// it and the caller owns the wait (wait_vmem() and a barrier) before reading.
+__device__ __forceinline__ void copy16_async(void* lds_block, const void* src) {
+  const uint32_t dst =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds_block);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(dst), "v"(src)
+      : "memory");
+}
+
 // Wave-uniform copy of an int read from LDS (lets the compiler keep it scalar).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -337,6 +356,27 @@ __device__ __forceinline__ void put(float* p, float v) {
     *p += v;
   else
     *p = v;
+}
+
+// Fusion-weight softmax backward for one query chunk, run by one whole wave
+// with lane i holding slot i (lanes >= topk pass ok = false): dscore_i =
+// w_i (dw_i - sum_l w_l dw_l) over the valid slots, 0 on empty ones.  Lanes
+// < topk write dw_i and dscore_i (ACC: add them) and, in ACC mode, this
+// layer's dscore_i to ds_layer for the key side.  Returns dscore_i.
+template <bool ACC>
+__device__ __forceinline__ float slot_dscore(int lane, int topk, bool ok, float w_lane,
+                                             float dw_lane, float* __restrict__ dw_out,
+                                             float* __restrict__ dscore_out,
+                                             float* __restrict__ ds_layer) {
+  const float dwv = ok ? dw_lane : 0.0f;
+  const float sw = wave_sum(ok ? w_lane * dwv : 0.0f);
+  const float ds = ok ? w_lane * (dwv - sw) : 0.0f;
+  if (lane < topk) {
+    put<ACC>(dw_out + lane, dwv);
+    put<ACC>(dscore_out + lane, ds);
+    if (ACC) ds_layer[lane] = ds;
+  }
+  return ds;
 }
 
 __device__ __forceinline__ float load_f(const float* p) { return *p; }
