@@ -462,7 +462,7 @@ __device__ __forceinline__ void bwdkv_fetch(const BwdKVCtx<D>& cx, int u, KVNext
     nx.row = tid < 64 ? cx.lse_head[(int64_t)ent * 64 + tid]
                       : cx.d_head[(int64_t)ent * 64 + (tid - 64)];
   nx.w = cx.w_head[ent];
-  if (cx.lq_head) {
+  if (cx.lq_head && tid < 64) {  // wave 0 carries dlk (dl <= 64)
     nx.ds = cx.ds_head[ent];
     nx.lq = cx.lq_head[(int64_t)t * cx.dl + (tid < cx.dl ? tid : 0)];
   }
