@@ -151,7 +151,6 @@ def measure_peaks(reps=10):
     t_read = timed(lambda: gca.gca_peak_read(src, out))
     dst = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
     t_copy = timed(lambda: gca.gca_peak_copy(src[:n_copy], dst))
-    del src, dst
     mf = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
     flops = [0.0]
 
@@ -159,12 +158,26 @@ def measure_peaks(reps=10):
         flops[0] = gca.gca_peak_mfma(mf, 2048)
 
     t_mfma = timed(mfma)
+    # tile gathers into LDS from a buffer that every XCD's L2 holds (2 MiB), one that
+    # only the last-level cache holds (32 MiB) and one from HBM (1 GiB)
+    gout = torch.empty(gca.PEAK_GATHER_OUT_BYTES, dtype=torch.uint8, device="cuda")
+    moved = [0.0]
+    gather = {}
+    for label, size, iters in (("l2", 2 << 20, 64), ("llc", 32 << 20, 16), ("hbm", 1 << 30, 16)):
+        def gfn(size=size, iters=iters):
+            moved[0] = gca.gca_peak_gather(src[:size], gout, iters)
+        t = timed(gfn)
+        gather[f"gather_{label}_GBps"] = round(moved[0] / t / 1e9, 1)
+    del src, dst
     torch.cuda.empty_cache()
     return {"hbm_read_GBps": round(n_read / t_read / 1e9, 1),
             "copy_read_plus_write_GBps": round(2 * n_copy / t_copy / 1e9, 1),
             "mfma_bf16_dense_TFLOPs": round(flops[0] / t_mfma / 1e12, 1),
+            **gather,
             "note": "gca_peak_read (2 GiB), gca_peak_copy (1 GiB), gca_peak_mfma (16x16x32 "
-                    "bf16, 4 waves per SIMD, 8 independent accumulators per wave)"}
+                    "bf16, 4 waves per SIMD, 8 independent accumulators per wave), "
+                    "gca_peak_gather (random 16 KB tiles into LDS, one in flight per "
+                    "workgroup, 4 workgroups per CU; from 2 MiB, 32 MiB and 1 GiB buffers)"}
 
 
 def with_measured(entry, peaks):
@@ -946,7 +959,9 @@ def main():
     peaks = measure_peaks()
     print(f"[bench] measured peaks: {peaks['hbm_read_GBps']} GB/s read, "
           f"{peaks['copy_read_plus_write_GBps']} GB/s copy, "
-          f"{peaks['mfma_bf16_dense_TFLOPs']} TFLOP/s bf16 MFMA", file=sys.stderr, flush=True)
+          f"{peaks['mfma_bf16_dense_TFLOPs']} TFLOP/s bf16 MFMA, tile gather "
+          f"{peaks['gather_l2_GBps']} / {peaks['gather_llc_GBps']} / {peaks['gather_hbm_GBps']} "
+          f"GB/s (L2 / last-level cache / HBM)", file=sys.stderr, flush=True)
     roof = with_measured(roofline_entry(dom, kernels[dom]["avg_us"] * 1e-6, work[dom]), peaks)
     sw = step_work(cfg, pairs)
     t_step_roof = max(sw["bytes"] / HBM_PEAK, sw["flops"] / MFMA_BF16_PEAK)
@@ -973,6 +988,13 @@ def main():
                               peaks)
             kernels[name].update(bound=e["bound"], frac=e["frac"],
                                  frac_of_measured_peak=e["frac_of_measured_peak"])
+    gathered = S * D * 2 * 2 * pairs  # K and V (or Q and dO) tiles of every pair
+    for name in ("forward", "backward_q", "backward_kv"):
+        if name in kernels:
+            rate = gathered / (kernels[name]["avg_us"] * 1e-6) / 1e9
+            kernels[name].update(gathered_GB=round(gathered / 1e9, 3),
+                                 gather_GBps=round(rate, 1),
+                                 frac_of_l2_gather_peak=round(rate / peaks["gather_l2_GBps"], 4))
     print(f"[bench] timed {args.steps} steps: {step_ms:.3f} ms/step, dominant {dom}",
           file=sys.stderr, flush=True)
     if args.copy_ref > 0:

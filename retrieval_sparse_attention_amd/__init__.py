@@ -47,8 +47,9 @@ EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_works
             "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
             "gca_swa_forward", "gca_swa_backward")
 # include/gca_peaks.h: microbenchmarks for the peaks measured on the GPU at hand
-PEAK_EXPORTED = ("gca_peak_read", "gca_peak_copy", "gca_peak_mfma")
+PEAK_EXPORTED = ("gca_peak_read", "gca_peak_copy", "gca_peak_gather", "gca_peak_mfma")
 PEAK_OUT_BYTES = 2048 * 256 * 4
+PEAK_GATHER_OUT_BYTES = 4096 * 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -139,6 +140,9 @@ def load():
     lib.gca_peak_read.restype = ctypes.c_int
     lib.gca_peak_copy.argtypes = [vp, vp, sz, vp]
     lib.gca_peak_copy.restype = ctypes.c_int
+    lib.gca_peak_gather.argtypes = [vp, sz, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                    vp]
+    lib.gca_peak_gather.restype = ctypes.c_int
     lib.gca_peak_mfma.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double), vp]
     lib.gca_peak_mfma.restype = ctypes.c_int
     lib.gca_num_kernels.argtypes = []
@@ -334,6 +338,16 @@ def gca_peak_copy(src, dst):
     """Streaming copy of src's bytes into dst (same size, device tensors)."""
     _check(load().gca_peak_copy(_ptr(src, "src"), _ptr(dst, "dst"),
                                 ctypes.c_size_t(src.numel() * src.element_size()), _stream()))
+
+
+def gca_peak_gather(src, out, iters):
+    """Gather of 16 KB tiles picked among src's bytes into LDS; returns the bytes moved.
+    out: >= PEAK_GATHER_OUT_BYTES."""
+    moved = ctypes.c_double(0.0)
+    _check(load().gca_peak_gather(_ptr(src, "src"),
+                                  ctypes.c_size_t(src.numel() * src.element_size()),
+                                  _ptr(out, "out"), int(iters), ctypes.byref(moved), _stream()))
+    return moved.value
 
 
 def gca_peak_mfma(out, iters):

@@ -659,6 +659,20 @@ gca_status gca_peak_copy(const void* src, void* dst, size_t bytes, void* stream)
   return device_status(gca::launch_peak_copy(src, dst, bytes, st), st, "gca_peak_copy");
 }
 
+gca_status gca_peak_gather(const void* src, size_t bytes, void* out, int iters, double* gathered,
+                           void* stream) {
+  GCA_TRY(need(src, "src", 16));
+  GCA_TRY(need(out, "out", 4));
+  if (bytes < 16384 || bytes % 16384 != 0)
+    return fail(GCA_ERR_INVALID_ARGUMENT,
+                "gca_peak_gather: bytes must be a positive multiple of 16384");
+  if (iters < 1 || iters > 4096)
+    return fail(GCA_ERR_INVALID_ARGUMENT, "gca_peak_gather: iters must be in 1 .. 4096");
+  if (gathered) *gathered = 4096.0 * (double)iters * 16384.0;
+  hipStream_t st = (hipStream_t)stream;
+  return device_status(gca::launch_peak_gather(src, bytes, out, iters, st), st, "gca_peak_gather");
+}
+
 gca_status gca_peak_mfma(void* out, int iters, double* flops, void* stream) {
   GCA_TRY(need(out, "out", 4));
   if (iters < 1 || iters > (1 << 20))

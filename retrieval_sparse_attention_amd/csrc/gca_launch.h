@@ -149,6 +149,8 @@ hipError_t launch_backward(const LaunchBackward& a);
 hipError_t launch_forward_s16(const LaunchForward& a, int64_t tiles);
 hipError_t launch_peak_read(const void* src, size_t bytes, void* out, hipStream_t stream);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_peak_gather(const void* src, size_t bytes, void* out, int iters,
+                              hipStream_t stream);
 hipError_t launch_peak_mfma(void* out, int iters, hipStream_t stream);
 hipError_t launch_backward_s16(const LaunchBackward& a, int64_t qtiles, int64_t ktiles);
 hipError_t launch_gather_kv(const LaunchGather& a);

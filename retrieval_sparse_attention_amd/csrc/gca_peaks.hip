@@ -1,8 +1,10 @@
 // Microbenchmarks for the peaks measured on the GPU at hand (include/gca_peaks.h):
-// a streaming read, a streaming copy and a loop of independent 16x16x32 bf16
-// MFMAs.  Grids are fixed: 2048 workgroups of 256 threads for the memory
-// kernels (eight per CU on 256 CUs), 1024 for the MFMA loop (four waves per
-// SIMD).  They share no arithmetic with the GCA kernels.
+// a streaming read, a streaming copy, a gather of 16 KB tiles into LDS and a
+// loop of independent 16x16x32 bf16 MFMAs.  Grids are fixed: 2048 workgroups
+// of 256 threads for the streaming kernels (eight per CU on 256 CUs), 4096 for
+// the gather (four resident per CU, as the attention kernels), 1024 for the
+// MFMA loop (four waves per SIMD).  They share no arithmetic with the GCA
+// kernels.
 
 #include "gca_device.h"
 #include "gca_launch.h"
@@ -11,6 +13,7 @@ namespace gca {
 
 constexpr int kPeakMemBlocks = 2048;
 constexpr int kPeakMfmaBlocks = 1024;
+constexpr int kPeakGatherBlocks = 4096;
 
 // Each workgroup streams one contiguous range (whole DRAM pages, one open
 // stream per workgroup); every thread keeps kPeakU 16-byte loads in flight and
@@ -60,6 +63,36 @@ __global__ __launch_bounds__(256) void k_peak_copy(const uint4* __restrict__ src
   for (; i < end; i += 256) dst[i] = src[i];
 }
 
+// Each workgroup moves `iters` tiles of 16 KB (the K and V tiles of one 64 x 64
+// bf16 chunk), picked by a per-workgroup linear congruential sequence among the
+// n_tiles of the buffer, into LDS with 16-byte global_load_lds: every wave
+// copies 4 KB of the tile, waits, and the workgroup meets at a barrier before
+// the next tile (one tile in flight, as the attention kernels' slot loop).  36 KB
+// of LDS per workgroup: four resident per CU.  Each workgroup writes one word
+// of its last tile, so no copy can be dropped.
+__global__ __launch_bounds__(256) void k_peak_gather(const char* __restrict__ src, int64_t n_tiles,
+                                                     int iters, uint32_t* __restrict__ out) {
+  __shared__ __align__(16) uint32_t buf[2][4096];
+  __shared__ uint32_t pad[1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint32_t h = (uint32_t)blockIdx.x * 2654435761u + 12345u;
+  for (int it = 0; it < iters; ++it) {
+    h = h * 1664525u + 1013904223u;
+    const char* tile = src + (int64_t)((h >> 8) % (uint64_t)n_tiles) * 16384;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = wave * 4 + p;  // 1 KB pieces, 16 per tile
+      __builtin_amdgcn_global_load_lds((const void*)(tile + piece * 1024 + lane * 16),
+                                       (lds_void*)(&buf[it & 1][piece * 256]), 16, 0, 0);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (tid == 0) pad[0] = buf[(iters - 1) & 1][h & 4095];
+  __syncthreads();
+  if (tid == 0) out[blockIdx.x] = pad[0];
+}
+
 // Eight accumulators per wave, each updated once per round: consecutive MFMAs
 // never depend on each other, so the matrix pipe issues back to back.
 __global__ __launch_bounds__(256) void k_peak_mfma(float* __restrict__ out, int iters) {
@@ -92,6 +125,13 @@ hipError_t launch_peak_read(const void* src, size_t bytes, void* out, hipStream_
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   hipLaunchKernelGGL(k_peak_copy, dim3(kPeakMemBlocks), dim3(256), 0, stream, (const uint4*)src,
                      (uint4*)dst, (int64_t)(bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_gather(const void* src, size_t bytes, void* out, int iters,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(k_peak_gather, dim3(kPeakGatherBlocks), dim3(256), 0, stream,
+                     (const char*)src, (int64_t)(bytes / 16384), iters, (uint32_t*)out);
   return hipGetLastError();
 }
 

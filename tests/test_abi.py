@@ -41,6 +41,14 @@ def test_peak_calls_reject_bad_arguments():
     assert st == 1 and "overlap" in msg
     st, msg = _status("gca_peak_mfma", A, 0, None, None)
     assert st == 1 and "iters" in msg
+    st, msg = _status("gca_peak_gather", A, ctypes.c_size_t(16384 + 16), A, 1, None, None)
+    assert st == 1 and "multiple of 16384" in msg
+    st, msg = _status("gca_peak_gather", A, ctypes.c_size_t(16384), A, 4097, None, None)
+    assert st == 1 and "iters" in msg
+    st, msg = _status("gca_peak_gather", A, ctypes.c_size_t(16384), None, 1, None, None)
+    assert st == 1 and "out is NULL" in msg
+    assert "4096 * 4" in open(PEAKS_HEADER).read()
+    assert gca.PEAK_GATHER_OUT_BYTES == 4096 * 4
     assert "2048 * 256 * 4" in open(PEAKS_HEADER).read()
     assert gca.PEAK_OUT_BYTES == 2048 * 256 * 4
 
