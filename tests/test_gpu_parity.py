@@ -261,33 +261,38 @@ def test_bf16_forward_invalid_and_duplicate_slots():
     assert (f64(o)[0, 0, 0, 1] == 0).all()
 
 
-@pytest.mark.parametrize("H,n_query", [(1, 4), (3, 100), (4, 250)],
-                         ids=["4_chunks", "300_chunks", "1000_chunks"])
-def test_bf16_forward_valid_slot_counts(H, n_query):
-    """Rows with every count of valid slots from 0 to 8, the others empty (-1)
-    or out of range, and repeated chunks, at a few query-chunk counts: O and
-    LSE must match the oracle and repeat bit for bit."""
+@pytest.mark.parametrize("H,n_query,k,D", [
+    (1, 4, 8, 64), (3, 100, 8, 64), (4, 250, 8, 64),
+    (1, 4, 16, 64), (2, 100, 16, 64), (3, 100, 16, 32), (1, 200, 12, 32), (2, 128, 3, 32)],
+    ids=["4_chunks", "300_chunks", "1000_chunks", "4_chunks_k16", "200_chunks_k16",
+         "300_chunks_k16_d32", "200_chunks_k12_d32", "256_chunks_k3_d32"])
+def test_bf16_forward_valid_slot_counts(H, n_query, k, D):
+    """Rows with every count of valid slots from 0 to k, the others empty (-1)
+    or out of range, and repeated chunks, at several query-chunk counts, k and
+    head_dim: O and LSE must match the oracle and repeat bit for bit."""
     n_key = 40
-    cfg = synth.workload("train16k_fwd", B=1, H=H, n_query=n_query, n_key=n_key)
-    rng = np.random.default_rng(H * 1000 + n_query)
+    cfg = synth.workload("train16k_fwd", B=1, H=H, n_query=n_query, n_key=n_key, k=k, D=D)
+    rng = np.random.default_rng(H * 1000 + n_query + 100000 * k + D)
     sc = cfg["value_scale"]
     mk = lambda *shape: torch.from_numpy(
         (rng.standard_normal(shape) * sc).astype(np.float32)).bfloat16()
-    q, k, v = mk(1, 1, H, n_query, 64, 64), mk(1, 1, H, n_key, 64, 64), mk(1, 1, H, n_key, 64, 64)
-    idx = rng.integers(0, n_key, size=(1, 1, H, n_query, 8)).astype(np.int32)
-    n_valid = rng.integers(0, 9, size=(1, 1, H, n_query))
-    m = min(9, n_valid.size)
+    q, kk, v = mk(1, 1, H, n_query, 64, D), mk(1, 1, H, n_key, 64, D), mk(1, 1, H, n_key, 64, D)
+    idx = rng.integers(0, n_key, size=(1, 1, H, n_query, k)).astype(np.int32)
+    n_valid = rng.integers(0, k + 1, size=(1, 1, H, n_query))
+    m = min(k + 1, n_valid.size)
     n_valid.reshape(-1)[:m] = np.arange(m)
     for pos in np.ndindex(n_valid.shape):
-        slots = rng.permutation(8)[n_valid[pos]:]
+        slots = rng.permutation(k)[n_valid[pos]:]
         idx[pos][slots] = np.where(rng.random(len(slots)) < 0.5, -1, n_key + 3)
-    rep = rng.random(idx.shape[:-1]) < 0.2
-    idx[..., 4][rep] = idx[..., 5][rep]
-    w = rng.random((1, 1, H, n_query, 8)).astype(np.float32)
+    if k >= 2:
+        rep = rng.random(idx.shape[:-1]) < 0.2
+        idx[..., k - 2][rep] = idx[..., k - 1][rep]
+    w = rng.random((1, 1, H, n_query, k)).astype(np.float32)
     shape = shape_of(cfg)
-    d = [dev(t) for t in (q, k, v, torch.from_numpy(idx), torch.from_numpy(w))]
+    d = [dev(t) for t in (q, kk, v, torch.from_numpy(idx), torch.from_numpy(w))]
     o, lse = run_forward(shape, *d)
-    r_o, r_lse = orc.forward(f64(q), f64(k), f64(v), idx, w.astype(np.float64), cfg["attn_scale"])
+    r_o, r_lse = orc.forward(f64(q), f64(kk), f64(v), idx, w.astype(np.float64),
+                             cfg["attn_scale"])
     close("o", f64(o), r_o, True)
     compare_lse(lse, r_lse, True)
     o2, lse2 = run_forward(shape, *d)
