@@ -25,7 +25,13 @@
 //   5. O^T += (w_i / l) V^T P^T: all k slots accumulate into ONE float32
 //      accumulator.  Each chunk's softmax is complete inside one 64-key tile:
 //      no running rescale is needed.
-// O is rounded to bf16 once at the end.
+// O is rounded to bf16 once at the end.  The workgroup's only LDS is the two
+// K/V tile buffers (32 KB at D = 64): every wave forms the slot table itself
+// from one ballot (lane i holds slot i's chunk and weight, read back with
+// readlane), the L rows stay in registers until the loop ends, and the V^T
+// operands are read right before their products.  At 92 registers five
+// workgroups then share a CU (20 waves against 16): on the 16K-token
+// two-group step the forward went from 352-354 to 341 us.
 //
 // Generic path (other sizes, float32 or bf16 elements).  One thread per query
 // row, float32 arithmetic, one rounding of the output (small workloads).
@@ -41,37 +47,37 @@ struct FwdCtx {
   const TileDma<4, D>* dma;
   const bf16* k_head;
   const bf16* v_head;
-  const int* s_c;      // LDS: chunk of each valid slot
-  const float* s_w;    // LDS: its fusion weight
-  const int* s_slot;   // LDS: its slot number
-  float* s_lse;        // LDS [16][64]: log-sum-exp rows, written out at the end
+  int c_lane;     // lane i: chunk of slot i (valid slots only)
+  float w_lane;   // lane i: fusion weight of slot i
   int x;
-  int n, lane, grp, col;
+  int lane, grp, col;
   float c2, attn_scale;
 };
 
-// DMA of the K and V tiles of valid slot u into kd / vd.
+// DMA of the K and V tiles of slot i into kd / vd.
 template <int D>
-__device__ __forceinline__ void fwd_issue(const FwdCtx<D>& cx, int u, bf16* __restrict__ kd,
+__device__ __forceinline__ void fwd_issue(const FwdCtx<D>& cx, int i, bf16* __restrict__ kd,
                                           bf16* __restrict__ vd) {
-  const int64_t c = uniform(cx.s_c[u]);
+  const int64_t c = __builtin_amdgcn_readlane(cx.c_lane, i);
   cx.dma->copy_async(kd, cx.k_head + c * (64 * D));
   cx.dma->copy_async(vd, cx.v_head + c * (64 * D));
 }
 
-// One retrieved chunk: kt/vt hold its tiles; the next chunk's tiles are sent
-// to kn/vn.  The restrict qualifiers tell the compiler that the LDS reads of
-// this chunk never touch the buffers being filled, so it does not wait for
-// that copy before reading (it would otherwise drain the copy at once).
+// One retrieved chunk (slot i, the u-th valid one; next: the next valid slot
+// or -1): kt/vt hold its tiles; the next chunk's tiles are sent to kn/vn.
+// The restrict qualifiers tell the compiler that the LDS reads of this chunk
+// never touch the buffers being filled, so it does not wait for that copy
+// before reading (it would otherwise drain the copy at once).
 template <int D>
-__device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, const bf16x8 (&bq)[D / 32],
-                                          f32x4 (&oacc)[D / 16], const bf16* __restrict__ kt,
+__device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, int i, int next,
+                                          const bf16x8 (&bq)[D / 32], f32x4 (&oacc)[D / 16],
+                                          float (&lsev)[4], const bf16* __restrict__ kt,
                                           const bf16* __restrict__ vt, bf16* __restrict__ kn,
                                           bf16* __restrict__ vn) {
   const int lane = cx.lane, grp = cx.grp, col = cx.col;
   wait_vmem();
-  __syncthreads();  // tiles of slot u are in LDS; slot u-1 is done with the other buffer
-  if (u + 1 < cx.n) fwd_issue(cx, u + 1, kn, vn);
+  __syncthreads();  // tiles of slot i are in LDS; the previous slot is done with the other buffer
+  if (next >= 0) fwd_issue(cx, next, kn, vn);
   // S^T = K Q^T: key tile mt (16 keys) x this wave's 16 queries; the lane
   // holds keys 16mt + 4*grp + r of its query column x.
   f32x4 sacc[4];
@@ -82,15 +88,6 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, const bf16
     for (int kd = 0; kd < D / 32; ++kd)
       sacc[mt] = mfma16x16x32(lds_row8<D>(kt, 16 * mt + col, 4 * kd + grp), bq[kd], sacc[mt]);
   }
-  // V^T operands of this slot, requested now so that the LDS latency overlaps
-  // the softmax arithmetic below.
-  bf16x8 va[2][D / 16];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      va[kb][dt] =
-          lds_tr_operand16<D>(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
   float m = max_nc(max_nc(sacc[0][0], sacc[1][0]), max_nc(sacc[2][0], sacc[3][0]));
 #pragma unroll
   for (int r = 1; r < 4; ++r)
@@ -102,9 +99,9 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, const bf16
 #pragma unroll
     for (int r = 0; r < 4; ++r) sacc[mt][r] = fast_exp2(fmaf(sacc[mt][r], cx.c2, -mb));
   // V^T P^T (d x x) of this chunk and its row sums 1^T P^T, both on MFMA from
-  // the same bf16 probabilities; K-step kb covers keys 32kb + 4*grp + 0..3
-  // (key tile 2kb) and 32kb + 16 + 4*grp + 0..3 (key tile 2kb+1): exactly what
-  // this lane holds; V^T comes by transpose reads.
+  // the same bf16 probabilities; K-step kb covers keys 32kb + 4*grp + 0..3 and
+  // 32kb + 16 + 4*grp + 0..3, exactly what this lane holds; V^T comes by
+  // transpose reads, each right before its product.
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
@@ -118,59 +115,54 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, const bf16
       bp[4 + e] = (bf16)sacc[2 * kb + 1][e];
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) pv[dt] = mfma16x16x32(va[kb][dt], bp, kb ? pv[dt] : zero4());
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const bf16x8 va =
+          lds_tr_operand16<D>(vt, 16 * dt, 32 * kb + 4 * grp, 32 * kb + 16 + 4 * grp, lane);
+      pv[dt] = mfma16x16x32(va, bp, kb ? pv[dt] : zero4());
+    }
     lacc = mfma16x16x32(ones, bp, lacc);
   }
   const float l = lacc[0];
-  if (grp == 0) cx.s_lse[uniform(cx.s_slot[u]) * 64 + cx.x] = cx.attn_scale * m + fast_ln(l);
+  // this slot's L row, kept by the lanes with grp == u % 4 (every lane of the
+  // column holds m and l) and stored after the loop
+  const float lv = cx.attn_scale * m + fast_ln(l);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lsev[j] = (u == 4 * j + grp) ? lv : lsev[j];
   // O^T += (w_i / l) V^T P^T: the fusion weight and the normalisation in one factor
-  const float ps = cx.s_w[u] * fast_rcp(l);
+  const float ps = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cx.w_lane), i)) *
+                   fast_rcp(l);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(ps, pv[dt][e], oacc[dt][e]);
 }
 
+// Lowest set bit of m above bit i, or -1: the valid slot after slot i.
+__device__ __forceinline__ int next_slot(uint32_t m, int i) {
+  const uint32_t rest = i >= 31 ? 0u : (m & ~((2u << i) - 1u));
+  return rest ? (int)__builtin_ctz(rest) : -1;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_fwd_bf16(
+__global__ __launch_bounds__(256, 5) void k_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ o,
     float* __restrict__ lse, int64_t n_query, int64_t n_key, int topk, float attn_scale) {
   __shared__ __align__(16) bf16 k_lds[2][64 * D];
   __shared__ __align__(16) bf16 v_lds[2][64 * D];
-  __shared__ int s_c[16];
-  __shared__ float s_w[16];
-  __shared__ int s_slot[16];
-  __shared__ int s_n;
-  __shared__ int s_mask;
-  // Log-sum-exp rows of the k slots, staged here and stored once at the end:
-  // a store per chunk would be waited on by the next chunk's copy wait.
-  __shared__ float s_lse[16 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
   const int64_t head = tile / n_query;
   const int x = 16 * wave + col;  // query row owned by this lane
-  for (int e = tid; e < topk * 64; e += 256) s_lse[e] = -__builtin_huge_valf();  // empty slots
 
-  // compact list of the valid slots, built in one step from a wave ballot
-  if (wave == 0) {
-    const int i = lane < topk ? lane : 0;
-    const int c = idx[tile * topk + i];
-    const float wv = w[tile * topk + i];
-    const bool ok = lane < topk && c >= 0 && c < n_key;
-    const uint64_t mask = __ballot(ok);
-    if (ok) {
-      const int pos = __popcll(mask & ((1ull << lane) - 1));
-      s_c[pos] = c;
-      s_w[pos] = wv;
-      s_slot[pos] = lane;
-    }
-    if (lane == 0) {
-      s_n = __popcll(mask);
-      s_mask = (int)mask;
-    }
-  }
+  // every wave reads the slot table itself: lane i holds slot i
+  const int i0 = lane < topk ? lane : 0;
+  const int c_in = idx[tile * topk + i0];
+  const float w_in = w[tile * topk + i0];
+  const bool ok = lane < topk && c_in >= 0 && c_in < n_key;
+  const uint32_t mask = (uint32_t)__ballot(ok);  // topk <= 16
+  const int n = __popc(mask);
   bf16x8 bq[D / 32];  // Q^T as the B operand: column x, dims 32*kd + 8*grp + 0..7
   {
     const bf16* row = q + tile * (64 * D) + x * D + 8 * grp;
@@ -180,35 +172,51 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = zero4();
+  float lsev[4];  // L rows of the valid slots with ordinal 4j + grp (topk <= 16)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lsev[j] = 0.0f;
   const TileDma<4, D> dma(wave, lane);
   FwdCtx<D> cx;
   cx.dma = &dma;
   cx.k_head = kk + head * n_key * (64 * D);
   cx.v_head = v + head * n_key * (64 * D);
-  cx.s_c = s_c;
-  cx.s_w = s_w;
-  cx.s_slot = s_slot;
-  cx.s_lse = s_lse;
+  cx.c_lane = ok ? c_in : 0;
+  cx.w_lane = w_in;
   cx.x = x;
   cx.lane = lane;
   cx.grp = grp;
   cx.col = col;
   cx.c2 = attn_scale * kLog2e;
   cx.attn_scale = attn_scale;
-  __syncthreads();
-  const int n = uniform(s_n);
-  cx.n = n;
-  if (n > 0) fwd_issue(cx, 0, k_lds[0], v_lds[0]);
+  int i = mask ? (int)__builtin_ctz(mask) : -1;
+  if (i >= 0) fwd_issue(cx, i, k_lds[0], v_lds[0]);
   // unrolled by two: each step's buffers are fixed LDS addresses
   for (int u = 0; u < n; u += 2) {
-    fwd_chunk(cx, u, bq, oacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
-    if (u + 1 < n) fwd_chunk(cx, u + 1, bq, oacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+    int nx = next_slot(mask, i);
+    fwd_chunk(cx, u, i, nx, bq, oacc, lsev, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
+    i = nx;
+    if (u + 1 < n) {
+      nx = next_slot(mask, i);
+      fwd_chunk(cx, u + 1, i, nx, bq, oacc, lsev, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+      i = nx;
+    }
   }
   if (lse) {
-    __syncthreads();
-    for (int e = tid; e < topk * 64; e += 256) lse[tile * topk * 64 + e] = s_lse[e];
+    float* lt = lse + tile * topk * 64;
+    for (int e = lane; e < topk * 16; e += 64) {  // empty slots of this wave's 16 rows
+      const int s = e >> 4;
+      if (!((mask >> s) & 1)) lt[s * 64 + 16 * wave + (e & 15)] = -__builtin_huge_valf();
+    }
+    // valid slot with ordinal 4j + grp: its L row for this lane's query row
+    int ord = 0;
+    for (int s = 0; s < topk; ++s) {
+      if (!((mask >> s) & 1)) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ord == 4 * j + grp) lt[s * 64 + x] = lsev[j];
+      ++ord;
+    }
   }
-  // O[x][d]: this lane holds d = 16dt + 4*grp + 0..3 for its row x.
   bf16* orow = o + tile * (64 * D) + x * D + 4 * grp;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
