@@ -283,6 +283,13 @@ __device__ __forceinline__ void copy16_async(void* lds_block, const void* src) {
       : "memory");
 }
 
+// Valid-slot iteration over a wave's ballot of valid slots (bit i: slot i):
+// the lowest set bit above bit i, or -1.
+__device__ __forceinline__ int next_slot(uint32_t m, int i) {
+  const uint32_t rest = i >= 31 ? 0u : (m & ~((2u << i) - 1u));
+  return rest ? (int)__builtin_ctz(rest) : -1;
+}
+
 // Wave-uniform copy of an int read from LDS (lets the compiler keep it scalar).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

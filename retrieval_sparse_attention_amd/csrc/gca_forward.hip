@@ -137,12 +137,6 @@ __device__ __forceinline__ void fwd_chunk(const FwdCtx<D>& cx, int u, int i, int
     for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(ps, pv[dt][e], oacc[dt][e]);
 }
 
-// Lowest set bit of m above bit i, or -1: the valid slot after slot i.
-__device__ __forceinline__ int next_slot(uint32_t m, int i) {
-  const uint32_t rest = i >= 31 ? 0u : (m & ~((2u << i) - 1u));
-  return rest ? (int)__builtin_ctz(rest) : -1;
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 5) void k_fwd_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ v,
