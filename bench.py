@@ -359,6 +359,23 @@ def cpu_baselines(pool, workers):
     return out
 
 
+def _latency(fn, reps):
+    """Average ms of fn() over reps calls on the current stream, with the library's
+    per-kernel event timing off."""
+    import torch
+
+    import retrieval_sparse_attention_amd as gca
+    gca.gca_timing_enable(False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def _timed(fn, reps):
     """Average ms of fn() over reps calls, on the current stream, plus per-kernel sums."""
     import torch
@@ -618,16 +635,27 @@ def bench_retrieve16m(reps=20, inp=None):
     ws = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)), dtype=torch.uint8,
                      device="cuda")
 
-    def step():
+    def two_calls():
         gca.gca_retrieve(shape, lqd, lkd, qpos, idx, score, w, ws=ws)
         gca.gca_forward(shape, qd, kd, vd, idx, w, o, lse)
 
+    def one_call():  # the slice merge runs inside the forward's kernel
+        gca.gca_retrieve_forward(shape, lqd, lkd, qpos, qd, kd, vd, idx, score, w, o, lse, ws=ws)
+
     for _ in range(3):
-        step()
-    ms, per = _timed(step, reps)
+        two_calls()
+    _, per2 = _timed(two_calls, reps)
+    ms2 = _latency(two_calls, reps)
+    ref = [t.clone() for t in (idx, score, w, o, lse)]
+    for _ in range(3):
+        one_call()
+    _, per = _timed(one_call, reps)
+    ms = _latency(one_call, reps)
+    same = all(torch.equal(a, b) for a, b in zip(ref, (idx, score, w, o, lse)))
     scan_ms = per.get("scan_topk", 0.0)
-    merge_ms = per.get("topk_merge", 0.0)
-    fwd_ms = per.get("forward", 0.0)
+    merge_ms = per2.get("topk_merge", 0.0)
+    fwd_ms = per2.get("forward", 0.0)
+    mf_ms = per.get("topk_merge_forward", 0.0)
     lk_bytes = G * B * H * Nk * cfg["Dl"] * 2
     scores = G * B * H * Nq * Nk
     best = torch.gather(idx, -1, score.argmax(-1, keepdim=True))[..., 0].cpu()
@@ -636,13 +664,16 @@ def bench_retrieve16m(reps=20, inp=None):
     torch.cuda.empty_cache()
     return {"workload": name, "tokens": Nk * cfg["S"], "query_chunks": Nq, "heads": H,
             "retrieve_fwd_latency_ms": round(ms, 4),
-            "scan_us": round(scan_ms * 1e3, 2), "merge_us": round(merge_ms * 1e3, 2),
-            "forward_us": round(fwd_ms * 1e3, 2),
+            "call": "gca_retrieve_forward (slice merge inside the forward's kernel)",
+            "retrieve_then_forward_latency_ms": round(ms2, 4),
+            "one_call_equals_two_calls_bits": bool(same),
+            "scan_us": round(scan_ms * 1e3, 2), "merge_forward_us": round(mf_ms * 1e3, 2),
+            "merge_us": round(merge_ms * 1e3, 2), "forward_us": round(fwd_ms * 1e3, 2),
             "landmark_scan_GBps": round(lk_bytes / (scan_ms * 1e-3) / 1e9, 1) if scan_ms else None,
             "landmark_scan_roofline_frac": round(lk_bytes / (scan_ms * 1e-3) / HBM_PEAK, 4)
             if scan_ms else None,
             "topk_scores_per_s": round(scores / ((scan_ms + merge_ms) * 1e-3), 1)
-            if scan_ms else None,
+            if scan_ms and merge_ms else None,
             "needle_hit_rate": hits, "reps": reps}
 
 
@@ -675,29 +706,39 @@ def bench_infer1m(steps, inp=None):
     ws = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)), dtype=torch.uint8,
                      device="cuda")
 
-    def step(s):
+    def step(s):  # retrieval + forward in one call (the merge inside the forward's kernel)
+        gca.gca_retrieve_forward(shape, lqs[s], lkd, qpos, qs[s], kd, vd, idx[s], score[s], w[s],
+                                 o[s], lse[s], ws=ws)
+
+    def step_two_calls(s):
         gca.gca_retrieve(shape, lqs[s], lkd, qpos, idx[s], score[s], w[s], ws=ws)
         gca.gca_forward(shape, qs[s], kd, vd, idx[s], w[s], o[s], lse[s])
 
-    for s in range(10):
-        step(s)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
-    for s in range(steps):
-        step(s)
-        ev[s + 1].record()
-    torch.cuda.synchronize()
-    lat = np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]) * 1e3
+    def latencies(fn):
+        for s in range(10):
+            fn(s)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for s in range(steps):
+            fn(s)
+            ev[s + 1].record()
+        torch.cuda.synchronize()
+        return np.array([ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]) * 1e3
+
+    lat2 = latencies(step_two_calls)
+    lat = latencies(step)
     best = torch.gather(idx, -1, score.argmax(-1, keepdim=True))[..., 0, 0].cpu()
     hits = float((best == needles.view(steps, 1, 1, 1)).float().mean())
     graph = bench_infer1m_graph(shape, lqs, qs, lkd, kd, vd, qpos, ws, idx, o, min(steps, 200))
     del kd, vd
     torch.cuda.empty_cache()
     return {"workload": name, "tokens": Nk * S, "steps": steps,
+            "call": "gca_retrieve_forward (slice merge inside the forward's kernel)",
             "step_latency_us_p50": round(float(np.percentile(lat, 50)), 2),
             "step_latency_us_p99": round(float(np.percentile(lat, 99)), 2),
             "step_latency_us_mean": round(float(lat.mean()), 2),
+            "two_calls_step_latency_us_p50": round(float(np.percentile(lat2, 50)), 2),
             "needle_hit_rate": hits, "hip_graph": graph}
 
 
@@ -721,8 +762,8 @@ def bench_infer1m_graph(shape, lqs, qs, lkd, kd, vd, qpos, ws, idx_eager, o_eage
 
     def body():
         for s in range(per_graph):
-            gca.gca_retrieve(shape, lqs[s], lkd, qpos, idx_g[s], score_g[s], w_g[s], ws=ws)
-            gca.gca_forward(shape, qs[s], kd, vd, idx_g[s], w_g[s], o_g[s], lse_g[s])
+            gca.gca_retrieve_forward(shape, lqs[s], lkd, qpos, qs[s], kd, vd, idx_g[s], score_g[s],
+                                     w_g[s], o_g[s], lse_g[s], ws=ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -310,6 +310,33 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k,
                        float* lse, void* stream);
 
 /*
+ * gca_retrieve_forward -- gca_retrieve followed by gca_forward in one call.
+ *
+ * Definition: as gca_retrieve and gca_forward (long-context-modeling README,
+ * "Model Architecture": a chunk retrieves its top-k past chunks, then attends
+ * to each and fuses the results), with the retrieval's idx and w feeding the
+ * forward.  The outputs are those of the two calls made in turn, bit for bit:
+ * idx, score, w as gca_retrieve writes them, o and lse as gca_forward writes
+ * them from that idx and w.
+ *
+ *   lq, lk, q_pos, idx, score, w  as for gca_retrieve (idx, score, w outputs)
+ *   q, k, v, o, lse               as for gca_forward
+ *   ws / ws_bytes                 workspace of the retrieval (gca_workspace_size
+ *                                 op 0); the forward needs none
+ *
+ * When the retrieval is cut into slices (long candidate lists) and the chunks
+ * are bf16 with chunk_size 64 and head_dim 64 or 32, the merge of the slices'
+ * lists runs inside the forward's kernel, which saves a launch and a round
+ * trip to memory on latency-bound steps (decoding, long-context retrieval).
+ * Every argument of both parts is checked before anything is launched; the
+ * conditions and error codes are those of gca_retrieve and gca_forward.
+ */
+gca_status gca_retrieve_forward(const gca_shape* shape, const void* lq, const void* lk,
+                                const int32_t* q_pos, const void* q, const void* k,
+                                const void* v, int32_t* idx, float* score, float* w, void* o,
+                                float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * gca_backward -- gradients of the forward and of the fusion weights/scores.
  *
  * Definition: paperlayer.ai summary, appendix B (the backward returns gradients

@@ -10,6 +10,7 @@ stream.  The entry points mirror the C ABI in include/gca.h:
   gca_retrieve_gumbel(shape, seed, lq, lk, q_pos, idx, score, w, ws=None)
   gca_gather_kv(shape, idx, k, v, k_packed, v_packed, idx_packed)   k, v may be pinned host
   gca_forward(shape, q, k, v, idx, w, o, lse=None)
+  gca_retrieve_forward(shape, lq, lk, q_pos, q, k, v, idx, score, w, o, lse=None, ws=None)
   gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,
                dlq=None, dlk=None, ws=None)
   gca_backward_accumulate(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk_acc, dv_acc,
@@ -30,7 +31,8 @@ __all__ = ["GCA_F32", "GCA_BF16", "GcaShape", "GcaError", "make_shape", "library
            "load", "gca_abi_version", "gca_status_string", "gca_last_error",
            "gca_workspace_size", "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel",
            "gca_gather_kv",
-           "gca_forward", "gca_backward", "gca_backward_accumulate", "GcaSwaShape",
+           "gca_forward", "gca_retrieve_forward", "gca_backward", "gca_backward_accumulate",
+           "GcaSwaShape",
            "make_swa_shape",
            "gca_swa_workspace_size", "gca_swa_forward", "gca_swa_backward",
            "OP_RETRIEVE", "OP_FORWARD", "OP_BACKWARD",
@@ -42,7 +44,7 @@ GCA_BF16 = 1
 OP_RETRIEVE, OP_FORWARD, OP_BACKWARD = 0, 1, 2
 EXPORTED = ("gca_abi_version", "gca_status_string", "gca_last_error", "gca_workspace_size",
             "gca_retrieve", "gca_retrieve_noalloc", "gca_retrieve_gumbel", "gca_gather_kv",
-            "gca_forward", "gca_backward", "gca_backward_accumulate",
+            "gca_forward", "gca_retrieve_forward", "gca_backward", "gca_backward_accumulate",
             "gca_num_kernels", "gca_kernel_name",
             "gca_timing_enable", "gca_timing_collect", "gca_swa_workspace_size",
             "gca_swa_forward", "gca_swa_backward")
@@ -124,6 +126,8 @@ def load():
     lib.gca_gather_kv.argtypes = [sp] + [vp] * 6 + [vp]
     lib.gca_forward.restype = ctypes.c_int
     lib.gca_forward.argtypes = [sp] + [vp] * 7 + [vp]
+    lib.gca_retrieve_forward.restype = ctypes.c_int
+    lib.gca_retrieve_forward.argtypes = [sp] + [vp] * 12 + [sz, vp]
     lib.gca_backward.restype = ctypes.c_int
     lib.gca_backward.argtypes = [sp] + [vp] * 16 + [vp, sz, vp]
     lib.gca_backward_accumulate.restype = ctypes.c_int
@@ -253,6 +257,17 @@ def gca_forward(shape, q, k, v, idx, w, o, lse=None):
     _check(load().gca_forward(
         ctypes.byref(shape), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(idx, "idx"),
         _ptr(w, "w"), _ptr(o, "o"), _ptr(lse, "lse"), _stream()))
+
+
+def gca_retrieve_forward(shape, lq, lk, q_pos, q, k, v, idx, score, w, o, lse=None, ws=None):
+    """gca_retrieve then gca_forward in one call (the slice merge fused into the forward
+    where the retrieval is sliced); ws: the retrieval's workspace (op 0)."""
+    ws = _workspace(shape, OP_RETRIEVE, ws, lq)
+    _check(load().gca_retrieve_forward(
+        ctypes.byref(shape), _ptr(lq, "lq"), _ptr(lk, "lk"), _ptr(q_pos, "q_pos"), _ptr(q, "q"),
+        _ptr(k, "k"), _ptr(v, "v"), _ptr(idx, "idx"), _ptr(score, "score"), _ptr(w, "w"),
+        _ptr(o, "o"), _ptr(lse, "lse"), _ptr(ws, "ws"),
+        ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size()), _stream()))
 
 
 def gca_backward(shape, q, k, v, idx, w, lse, dout, lq, lk, dq, dk, dv, dw, dscore,

@@ -257,7 +257,8 @@ gca_status gca_workspace_size(const gca_shape* shape, int op, size_t* bytes) {
 static gca_status retrieve_impl(const char* fn, const gca_shape* shape, int noise, uint64_t seed,
                                 const void* lq, const void* lk, const int32_t* q_pos,
                                 int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                void* stream, const gca::LaunchForward* fuse = nullptr,
+                                int* fused = nullptr) {
   Sizes z;
   GCA_TRY(check_shape(shape, kRetrieve, &z));
   // the bf16 scan prunes on unscaled dot products (ordered like r only for a
@@ -308,6 +309,8 @@ static gca_status retrieve_impl(const char* fn, const gca_shape* shape, int nois
   a.noise = noise;
   a.seed = seed;
   a.stream = (hipStream_t)stream;
+  a.fuse = fuse;
+  a.fused = fused;
   return device_status(gca::launch_retrieve(plan, a), a.stream, fn);
 }
 
@@ -488,8 +491,13 @@ gca_status gca_swa_backward(const gca_swa_shape* shape, const void* q, const voi
   return device_status(gca::launch_swa_backward(a), a.stream, "gca_swa_backward");
 }
 
-gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,
-                       const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
+// Checks of the forward's arguments and its launch description; *empty: no
+// query row (nothing to launch).  idx and w are checked only when check_slots
+// is set (the retrieval-plus-forward call writes them itself).
+static gca_status forward_args(const char* fn, const gca_shape* shape, const void* q,
+                               const void* k, const void* v, const int32_t* idx, const float* w,
+                               void* o, float* lse, void* stream, bool check_slots,
+                               gca::LaunchForward* a, bool* empty) {
   Sizes z;
   GCA_TRY(check_shape(shape, kForward, &z));
   // the bf16 MFMA kernels (chunk_size 64 or 16, head_dim 64 or 32) shift by the
@@ -497,41 +505,70 @@ gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, con
   // non-negative scale
   if (shape->dtype == GCA_BF16 && (shape->chunk_size == 64 || shape->chunk_size == 16) &&
       (shape->head_dim == 64 || shape->head_dim == 32) && shape->attn_scale < 0.0f)
-    return fail(GCA_ERR_UNSUPPORTED,
-                "gca_forward: bf16 attention on MFMA tiles needs attn_scale >= 0");
-  if (z.q_rows == 0) {
-    g_err[0] = '\0';
-    return GCA_OK;
-  }
+    return fail(GCA_ERR_UNSUPPORTED, "%s: bf16 attention on MFMA tiles needs attn_scale >= 0",
+                fn);
+  *empty = z.q_rows == 0;
+  if (*empty) return GCA_OK;
   GCA_TRY(need(q, "q", 16));
   if (shape->n_key > 0) {
     GCA_TRY(need(k, "k", 16));
     GCA_TRY(need(v, "v", 16));
   }
-  GCA_TRY(need(idx, "idx", 4));
-  GCA_TRY(need(w, "w", 4));
+  if (check_slots) {
+    GCA_TRY(need(idx, "idx", 4));
+    GCA_TRY(need(w, "w", 4));
+  }
   GCA_TRY(need(o, "o", 16));
   GCA_TRY(opt(lse, "lse", 4));
-  gca::LaunchForward a{};
-  a.G = shape->G;
-  a.B = shape->B;
-  a.H = shape->H;
-  a.n_query = shape->n_query;
-  a.n_key = shape->n_key;
-  a.S = shape->chunk_size;
-  a.D = shape->head_dim;
-  a.k = shape->top_k;
-  a.dtype = shape->dtype;
-  a.attn_scale = shape->attn_scale;
-  a.q = q;
-  a.kk = k;
-  a.v = v;
-  a.idx = idx;
-  a.w = w;
-  a.o = o;
-  a.lse = lse;
-  a.stream = (hipStream_t)stream;
+  *a = gca::LaunchForward{};
+  a->G = shape->G;
+  a->B = shape->B;
+  a->H = shape->H;
+  a->n_query = shape->n_query;
+  a->n_key = shape->n_key;
+  a->S = shape->chunk_size;
+  a->D = shape->head_dim;
+  a->k = shape->top_k;
+  a->dtype = shape->dtype;
+  a->attn_scale = shape->attn_scale;
+  a->q = q;
+  a->kk = k;
+  a->v = v;
+  a->idx = idx;
+  a->w = w;
+  a->o = o;
+  a->lse = lse;
+  a->stream = (hipStream_t)stream;
+  return GCA_OK;
+}
+
+gca_status gca_forward(const gca_shape* shape, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const float* w, void* o, float* lse, void* stream) {
+  gca::LaunchForward a;
+  bool empty = false;
+  GCA_TRY(forward_args("gca_forward", shape, q, k, v, idx, w, o, lse, stream, true, &a, &empty));
+  if (empty) {
+    g_err[0] = '\0';
+    return GCA_OK;
+  }
   return device_status(gca::launch_forward(a), a.stream, "gca_forward");
+}
+
+gca_status gca_retrieve_forward(const gca_shape* shape, const void* lq, const void* lk,
+                                const int32_t* q_pos, const void* q, const void* k,
+                                const void* v, int32_t* idx, float* score, float* w, void* o,
+                                float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "gca_retrieve_forward";
+  gca::LaunchForward f;
+  bool empty = false;
+  GCA_TRY(forward_args(fn, shape, q, k, v, idx, w, o, lse, stream, false, &f, &empty));
+  f.idx = idx;
+  f.w = w;
+  int fused = 0;
+  GCA_TRY(retrieve_impl(fn, shape, 0, 0, lq, lk, q_pos, idx, score, w, ws, ws_bytes, stream,
+                        &f, &fused));
+  if (empty || fused) return GCA_OK;
+  return device_status(gca::launch_forward(f), f.stream, fn);
 }
 
 static gca_status backward_impl(const char* fn, int accumulate, const gca_shape* shape,

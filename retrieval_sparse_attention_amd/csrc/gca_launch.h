@@ -18,6 +18,20 @@ struct ScanPlan {
                      // plain bf16 scan (k_scan_few_bf16); split_len is then 256
 };
 
+struct LaunchForward {
+  int64_t G, B, H, n_query, n_key;
+  int S, D, k, dtype;
+  float attn_scale;
+  const void* q;
+  const void* kk;
+  const void* v;
+  const int32_t* idx;
+  const float* w;
+  void* o;
+  float* lse;
+  hipStream_t stream;
+};
+
 struct LaunchRetrieve {
   int64_t G, B, H, n_query, n_key;
   int dl, k, dtype, softmax_one;
@@ -32,21 +46,14 @@ struct LaunchRetrieve {
   int noise;        // 1: Gumbel top-k (selection on r + G), 0: plain top-k
   uint64_t seed;    // Philox key of the Gumbel noise
   hipStream_t stream;
+  // Retrieval followed by the forward in one call: when set, a sliced plain
+  // retrieval at the 64-token tile sizes merges its slice lists inside the
+  // forward's kernel and sets *fused to 1; otherwise *fused stays 0 and the
+  // caller launches the forward.
+  const LaunchForward* fuse = nullptr;
+  int* fused = nullptr;
 };
 
-struct LaunchForward {
-  int64_t G, B, H, n_query, n_key;
-  int S, D, k, dtype;
-  float attn_scale;
-  const void* q;
-  const void* kk;
-  const void* v;
-  const int32_t* idx;
-  const float* w;
-  void* o;
-  float* lse;
-  hipStream_t stream;
-};
 
 struct LaunchBackward {
   int64_t G, B, H, n_query, n_key;
@@ -118,7 +125,8 @@ enum KernelId {
   kKernSwaForward = 7,
   kKernSwaBackwardQ = 8,
   kKernSwaBackwardKV = 9,
-  kNumKernels = 10
+  kKernMergeForward = 10,
+  kNumKernels = 11
 };
 
 // Records a HIP event pair around one kernel launch on `stream` when timing is

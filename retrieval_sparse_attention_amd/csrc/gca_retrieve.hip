@@ -28,6 +28,7 @@
 // the clean r of the selected chunks.
 
 #include "gca_device.h"
+#include "gca_fwd64.h"
 #include "gca_launch.h"
 
 namespace gca {
@@ -730,21 +731,25 @@ __global__ __launch_bounds__(256) void k_scan_few_bf16(
 // ---------------------------------------------------------------------------
 constexpr int kMergeMax = 4096;  // nsplit * KMAX limit (LDS list size)
 
-template <int KMAX, bool NOISE, int MW>
-__global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ part, int n,
-                                                   int k, int softmax_one,
-                                                   int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ score_out,
-                                                   float* __restrict__ w_out,
-                                                   const bf16* __restrict__ lq,
-                                                   const bf16* __restrict__ lk, int64_t n_query,
-                                                   int64_t n_key, int dl, float score_scale) {
-  __shared__ uint64_t lst[MW > 0 ? 64 * MW : kMergeMax];  // packed keys: at most n
-  __shared__ uint64_t out[KMAX];
-  __shared__ __align__(16) uint64_t lane_max[64];
-  __shared__ float clean[KMAX];  // with noise: clean scores of the selected
-  const int lane = threadIdx.x;
-  const int64_t qrow = blockIdx.x;
+// Barrier of the merge: the workgroup's when the workgroup is the merging wave
+// alone, else this wave's LDS order (the fused kernel merges in one wave).
+template <bool WG>
+__device__ __forceinline__ void merge_sync() {
+  if (WG)
+    __syncthreads();
+  else
+    wave_lds_sync();
+}
+
+// The merge of row qrow by one wave (lane = 0..63).  lst, out, lane_max and
+// clean are LDS areas of 64 MW (or kMergeMax), KMAX, 64 and KMAX entries;
+// the row's k slots go to idx_out / score_out / w_out + qrow * k.
+template <int KMAX, bool NOISE, int MW, bool WG>
+__device__ __forceinline__ void merge_row(
+    int lane, int64_t qrow, const uint64_t* __restrict__ part, int n, int k, int softmax_one,
+    int32_t* idx_out, float* score_out, float* w_out, const bf16* __restrict__ lq,
+    const bf16* __restrict__ lk, int64_t n_query, int64_t n_key, int dl, float score_scale,
+    uint64_t* lst, uint64_t* out, uint64_t* lane_max, float* clean) {
   const uint64_t* src = part + qrow * n;
 
   uint64_t mx = 0;
@@ -777,7 +782,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
   // by lane number), then the maximum of rank k-1; the 64 maxima go through
   // LDS once and come back as broadcast reads, all issued together
   lane_max[lane] = mx;
-  __syncthreads();
+  merge_sync<WG>();
   int rank = 0;
 #pragma unroll
   for (int l = 0; l < 64; l += 2) {
@@ -816,14 +821,14 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
       for (int u = 0; u < 4; ++u) pack(v[u]);
     }
   }
-  __syncthreads();
+  merge_sync<WG>();
   for (int i = lane; i < n2; i += 64) {
     const uint64_t me = lst[i];
     int r = 0;
     for (int f = 0; f < n2; ++f) r += lst[f] > me ? 1 : 0;
     if (r < k) out[r] = me;
   }
-  __syncthreads();
+  merge_sync<WG>();
   const int m = n2 < k ? n2 : k;
   if (NOISE) {
     if (lane < m) {
@@ -832,7 +837,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
                                   lk + (head * n_key + key_index(out[lane])) * dl, dl) *
                     score_scale;
     }
-    __syncthreads();
+    merge_sync<WG>();
   }
   if (lane == 0) {
     float s[KMAX];
@@ -845,6 +850,67 @@ __global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ 
     finalize_query<KMAX>(s, id, k, softmax_one, idx_out + qrow * k, score_out + qrow * k,
                          w_out + qrow * k);
   }
+}
+
+template <int KMAX, bool NOISE, int MW>
+__global__ __launch_bounds__(64) void k_topk_merge(const uint64_t* __restrict__ part, int n,
+                                                   int k, int softmax_one,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ score_out,
+                                                   float* __restrict__ w_out,
+                                                   const bf16* __restrict__ lq,
+                                                   const bf16* __restrict__ lk, int64_t n_query,
+                                                   int64_t n_key, int dl, float score_scale) {
+  __shared__ uint64_t lst[MW > 0 ? 64 * MW : kMergeMax];  // packed keys: at most n
+  __shared__ uint64_t out[KMAX];
+  __shared__ __align__(16) uint64_t lane_max[64];
+  __shared__ float clean[KMAX];  // with noise: clean scores of the selected
+  merge_row<KMAX, NOISE, MW, true>(threadIdx.x, blockIdx.x, part, n, k, softmax_one, idx_out,
+                                   score_out, w_out, lq, lk, n_query, n_key, dl, score_scale, lst,
+                                   out, lane_max, clean);
+}
+
+// ---------------------------------------------------------------------------
+// A sliced plain retrieval's merge fused with the 64-token forward (the
+// retrieval-plus-forward call): one 256-thread workgroup per query chunk, in
+// the forward's order.  Wave 0 merges the chunk's slice lists (n <= 64 MW
+// keys, held in registers) into the exact top k, which go to idx / score / w
+// and, through LDS, straight into the forward's slot table; the merge's key
+// list borrows the K tile buffers, which the forward fills only afterwards.
+// One launch and one round trip to memory fewer than the merge followed by
+// the forward, with the same results bit for bit.
+// ---------------------------------------------------------------------------
+template <int D, int KMAX, int MW>
+__global__ __launch_bounds__(256) void k_merge_fwd_bf16(
+    const uint64_t* __restrict__ part, int n, int k, int softmax_one, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out, float* __restrict__ w_out, const bf16* __restrict__ q,
+    const bf16* __restrict__ kk, const bf16* __restrict__ v, bf16* __restrict__ o,
+    float* __restrict__ lse, int64_t n_query, int64_t n_key, float attn_scale) {
+  static_assert(64 * MW * 8 <= 2 * 64 * D * 2, "the merge list fits the K tile buffers");
+  __shared__ __align__(16) bf16 k_lds[2][64 * D];
+  __shared__ __align__(16) bf16 v_lds[2][64 * D];
+  __shared__ uint64_t m_out[KMAX];
+  __shared__ __align__(16) uint64_t m_lane_max[64];
+  __shared__ int s_idx[16];
+  __shared__ float s_score[16], s_w[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // = head * n_query + t
+  if (tid < 64)
+    merge_row<KMAX, false, MW, false>(lane, 0, part + tile * n, n, k, softmax_one, s_idx, s_score,
+                                      s_w, nullptr, nullptr, n_query, n_key, 0, 0.0f,
+                                      (uint64_t*)&k_lds[0][0], m_out, m_lane_max, nullptr);
+  __syncthreads();
+  if (tid < k) {
+    idx_out[tile * k + tid] = s_idx[tid];
+    score_out[tile * k + tid] = s_score[tid];
+    w_out[tile * k + tid] = s_w[tid];
+  }
+  const int i0 = lane < k ? lane : 0;
+  const int c_in = s_idx[i0];
+  const float w_in = s_w[i0];
+  const bool ok = lane < k && c_in >= 0 && c_in < n_key;
+  fwd_tile<D>(q, kk, v, o, lse, tile, n_query, n_key, k, attn_scale, c_in, w_in, ok, k_lds,
+              v_lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -926,8 +992,24 @@ static hipError_t launch_scan_k(const ScanPlan& pl, const LaunchRetrieve& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nsplit == 1) return e;
     const int64_t rows = heads * a.n_query;
-    KernelTimer timer(kKernMerge, a.stream);
     const int n = pl.nsplit * KMAX;
+    const LaunchForward* f = a.fuse;
+    if (f && !NOISE && n <= 1024 && f->dtype == 1 && f->S == 64 && (f->D == 64 || f->D == 32)) {
+      KernelTimer timer(kKernMergeForward, a.stream);
+      auto fused = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(256), 0, a.stream, a.part, n, a.k,
+                           a.softmax_one, a.idx, a.score, a.w, (const bf16*)f->q,
+                           (const bf16*)f->kk, (const bf16*)f->v, (bf16*)f->o, f->lse,
+                           a.n_query, a.n_key, f->attn_scale);
+      };
+      if (f->D == 64)
+        n <= 512 ? fused(k_merge_fwd_bf16<64, KMAX, 8>) : fused(k_merge_fwd_bf16<64, KMAX, 16>);
+      else
+        n <= 512 ? fused(k_merge_fwd_bf16<32, KMAX, 8>) : fused(k_merge_fwd_bf16<32, KMAX, 16>);
+      if (a.fused) *a.fused = 1;
+      return hipGetLastError();
+    }
+    KernelTimer timer(kKernMerge, a.stream);
     auto merge = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(64), 0, a.stream, a.part, n, a.k,
                          a.softmax_one, a.idx, a.score, a.w, (const bf16*)a.lq,

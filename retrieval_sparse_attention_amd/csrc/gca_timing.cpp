@@ -44,7 +44,7 @@ hipEvent_t take_event(TimingState& s) {
 const char* kNames[kNumKernels] = {"scan_topk", "topk_merge", "forward",
                                    "reverse_index", "backward_q", "backward_kv",
                                    "gather_kv", "swa_forward", "swa_backward_q",
-                                   "swa_backward_kv"};
+                                   "swa_backward_kv", "topk_merge_forward"};
 
 }  // namespace
 

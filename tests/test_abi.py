@@ -153,6 +153,25 @@ def test_forward_rejects_null_and_misaligned():
     assert st == 1 and "o is NULL" in msg
 
 
+def test_retrieve_forward_checks_both_parts_before_any_device_call():
+    s = _bf16_shape(G=1, B=1, n_query=1, n_key=5000, softmax_one=0)
+    ws = ctypes.c_size_t(1 << 20)
+    # the forward's arguments are checked first, then the retrieval's
+    st, msg = _status("gca_retrieve_forward", ctypes.byref(s), A, A, A, A, A, A, A, A, A, None,
+                      None, A, ws, None)
+    assert st == 1 and "o is NULL" in msg
+    st, msg = _status("gca_retrieve_forward", ctypes.byref(s), A, A, None, A, A, A, A, A, A, A,
+                      None, A, ws, None)
+    assert st == 1 and "q_pos is NULL" in msg
+    st, msg = _status("gca_retrieve_forward", ctypes.byref(s), A, A, A, A, A, A, A, A, A, A,
+                      None, None, ctypes.c_size_t(0), None)
+    assert st == 3 and "workspace" in msg
+    neg = _bf16_shape(G=1, B=1, n_query=1, n_key=5000, attn_scale=-0.5)
+    st, msg = _status("gca_retrieve_forward", ctypes.byref(neg), A, A, A, A, A, A, A, A, A, A,
+                      None, A, ws, None)
+    assert st == 2 and "attn_scale >= 0" in msg
+
+
 def test_forwards_need_non_negative_attention_scale():
     # the bf16 forwards shift rows by the largest unscaled product
     s = _bf16_shape(attn_scale=-0.125)
