@@ -150,3 +150,53 @@ def test_retrieve_forward_rejects_before_launching():
         gca.gca_retrieve_forward(shape, lq, lk, q_pos, q, kv, kv, idx, score, w, None)
     torch.cuda.synchronize()
     assert (idx == -7).all()  # the retrieval did not run
+
+
+@pytest.mark.parametrize("dtype_name", ["tiny_fp32", "bf16_no_lse"])
+def test_retrieve_forward_other_paths(dtype_name):
+    """float32 (the VALU kernels: two launches) and a fused bf16 call without L
+    (lse = NULL): the same outputs as the two calls."""
+    if dtype_name == "tiny_fp32":
+        cfg = synth.workload("tiny_fp32")
+        x = synth.training_inputs("tiny_fp32", accept=None)
+    else:
+        cfg = synth.workload("infer1m_step", H=2, n_query=2, n_key=3000)
+        x = None
+    rng = np.random.default_rng(5)
+    G, B, H, nq, nk, S, D, Dl, k = (cfg[n] for n in ("G", "B", "H", "n_query", "n_key", "S",
+                                                     "D", "Dl", "k"))
+    bf = cfg["dtype"] == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+
+    def mk(*shape, scale):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).to(tdt)
+
+    if x is not None:
+        lq, lk, q, kk, v = x["lq"], x["lk"], x["q"], x["k"], x["v"]
+        q_pos = x["q_pos"].numpy()
+    else:
+        lq, lk = mk(G, B, H, nq, Dl, scale=1 / 8), mk(G, B, H, nk, Dl, scale=1 / 8)
+        q, kk, v = (mk(G, B, H, n, S, D, scale=cfg["value_scale"]) for n in (nq, nk, nk))
+        q_pos = np.full(nq, nk + 1, dtype=np.int32)
+    shape = shape_of(cfg)
+    d = {name: dev(t) for name, t in dict(lq=lq, lk=lk, q=q, k=kk, v=v,
+                                          q_pos=torch.from_numpy(q_pos)).items()}
+    slots = (G, B, H, nq, k)
+    i1 = torch.empty(slots, dtype=torch.int32, device="cuda")
+    s1, w1 = torch.empty(slots, device="cuda"), torch.empty(slots, device="cuda")
+    o1 = torch.empty(tuple(q.shape), dtype=tdt, device="cuda")
+    l1 = torch.empty(slots + (S,), device="cuda")
+    gca.gca_retrieve(shape, d["lq"], d["lk"], d["q_pos"], i1, s1, w1)
+    gca.gca_forward(shape, d["q"], d["k"], d["v"], i1, w1, o1, l1)
+    i2, s2, w2 = torch.full_like(i1, -7), torch.zeros_like(s1), torch.zeros_like(w1)
+    o2 = torch.zeros_like(o1)
+    lse2 = None if dtype_name == "bf16_no_lse" else torch.zeros_like(l1)
+    gca.gca_retrieve_forward(shape, d["lq"], d["lk"], d["q_pos"], d["q"], d["k"], d["v"], i2, s2,
+                             w2, o2, lse2)
+    torch.cuda.synchronize()
+    for name, a, b in (("idx", i1, i2), ("score", s1, s2), ("w", w1, w2), ("o", o1, o2)):
+        assert torch.equal(a, b), name
+    if lse2 is not None:
+        assert torch.equal(l1, lse2)
+    r_o, _ = orc.forward(f64(q), f64(kk), f64(v), i2.cpu().numpy(), f64(w2), cfg["attn_scale"])
+    close("o", f64(o2), r_o, bf)
