@@ -197,9 +197,8 @@ struct BwdQCtx {
   const TileDma<4, D>* dma;
   const bf16* k_head;
   const bf16* v_head;
-  const int* slot_c;   // LDS
-  const float* slot_w; // LDS
-  const int* s_list;   // LDS: valid slots in order
+  const int* slot_c;   // LDS: chunk of each slot
+  const float* slot_w; // LDS: its weight
   float (*dw_part)[16];  // LDS [4][16]
   const float* lse_row;  // lse + tile * topk * 64 + x
   float* s_delta;        // LDS [16][64]: D rows, written out at the end
@@ -209,21 +208,20 @@ struct BwdQCtx {
 };
 
 template <int D>
-__device__ __forceinline__ void bwdq_issue(const BwdQCtx<D>& cx, int u, bf16* __restrict__ kd,
+__device__ __forceinline__ void bwdq_issue(const BwdQCtx<D>& cx, int i, bf16* __restrict__ kd,
                                            bf16* __restrict__ vd) {
-  const int64_t c = uniform(cx.slot_c[uniform(cx.s_list[u])]);
+  const int64_t c = uniform(cx.slot_c[i]);
   cx.dma->copy_async(kd, cx.k_head + c * (64 * D));
   cx.dma->copy_async(vd, cx.v_head + c * (64 * D));
 }
 
 template <int D>
-__device__ __forceinline__ void bwdq_slot(const BwdQCtx<D>& cx, int u, float& l2_next,
+__device__ __forceinline__ void bwdq_slot(const BwdQCtx<D>& cx, int i, int nx, float& l2_next,
                                           const bf16x8 (&bq)[D / 32], const bf16x8 (&bdo)[D / 32],
                                           f32x4 (&dqacc)[D / 16], const bf16* __restrict__ kt,
                                           const bf16* __restrict__ vt, bf16* __restrict__ kn,
                                           bf16* __restrict__ vn) {
   const int lane = cx.lane, grp = cx.grp, col = cx.col;
-  const int i = uniform(cx.s_list[u]);
   const float wi = cx.slot_w[i];
   wait_vmem();
   __syncthreads();
@@ -232,9 +230,9 @@ __device__ __forceinline__ void bwdq_slot(const BwdQCtx<D>& cx, int u, float& l2
   // P_w = w P comes out of the exponential directly: log2 w joins the row's
   // offset (w = 0 gives P_w = 0 through exp2(-inf)).
   const float l2 = l2_next * kLog2e - __builtin_amdgcn_logf(wi);
-  if (u + 1 < cx.n) {
-    bwdq_issue(cx, u + 1, kn, vn);
-    l2_next = cx.lse_row[uniform(cx.s_list[u + 1]) * 64];
+  if (nx >= 0) {
+    bwdq_issue(cx, nx, kn, vn);
+    l2_next = cx.lse_row[nx * 64];
   }
   // S^T = K Q^T and dP~^T = V dO^T per key tile mt; lane holds keys 16mt + 4grp + r.
   f32x4 sacc[4], pacc[4];
@@ -302,7 +300,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   __shared__ int slot_c[16];
   __shared__ float slot_w[16];
   __shared__ float ds_slot[16];
-  __shared__ int s_list[16];
   __shared__ int s_n;
   __shared__ int s_mask;
   // D rows of the k slots, staged here and stored once at the end: a store per
@@ -317,7 +314,7 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   const int x = 16 * wave + col;
   for (int e = tid; e < topk * 64; e += 256) s_delta[e] = 0.0f;  // empty slots
 
-  if (wave == 0) {  // slot table and compact list of the valid slots, in one step
+  if (wave == 0) {  // slot table and the ballot of the valid slots, in one step
     const int i = lane < topk ? lane : 0;
     const int c = idx[tile * topk + i];
     const float wv = w[tile * topk + i];
@@ -327,7 +324,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
       slot_c[lane] = ok ? c : -1;
       slot_w[lane] = wv;
     }
-    if (ok) s_list[__popcll(mask & ((1ull << lane) - 1))] = lane;
     if (lane == 0) {
       s_n = __popcll(mask);
       s_mask = (int)mask;
@@ -354,7 +350,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   cx.v_head = v + head * n_key * (64 * D);
   cx.slot_c = slot_c;
   cx.slot_w = slot_w;
-  cx.s_list = s_list;
   cx.dw_part = dw_part;
   cx.lse_row = lse + tile * topk * 64 + x;
   cx.s_delta = s_delta;
@@ -366,10 +361,12 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
   cx.c2 = attn_scale * kLog2e;
   __syncthreads();
   const int n = uniform(s_n);
+  const uint32_t vmask = (uint32_t)uniform(s_mask);  // bit i: slot i valid
   cx.n = n;
   float l2_next = 0.0f;
+  int i = vmask ? (int)__builtin_ctz(vmask) : -1;  // slot of the u-th valid one
   if (n > 0) {
-    bwdq_issue(cx, 0, k_lds[0], v_lds[0]);
+    bwdq_issue(cx, i, k_lds[0], v_lds[0]);
     if (dlq && lk && wave < dl / 32) {
       // 16-byte piece e of the 16 x dl row block: row e / (dl / 8); rows of empty
       // slots and past topk take chunk 0 (their dscore is 0 or they are not read)
@@ -377,12 +374,17 @@ __global__ __launch_bounds__(256, 4) void k_bwd_q_bf16(
       const int c = r < topk && slot_c[r] >= 0 ? slot_c[r] : 0;
       copy16_async(lk_lds + wave * 512, lk + (head * n_key + c) * dl + (e % (dl / 8)) * 8);
     }
-    l2_next = cx.lse_row[uniform(s_list[0]) * 64];
+    l2_next = cx.lse_row[i * 64];
   }
   for (int u = 0; u < n; u += 2) {
-    bwdq_slot(cx, u, l2_next, bq, bdo, dqacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
-    if (u + 1 < n)
-      bwdq_slot(cx, u + 1, l2_next, bq, bdo, dqacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+    int nx = next_slot(vmask, i);
+    bwdq_slot(cx, i, nx, l2_next, bq, bdo, dqacc, k_lds[0], v_lds[0], k_lds[1], v_lds[1]);
+    i = nx;
+    if (u + 1 < n) {
+      nx = next_slot(vmask, i);
+      bwdq_slot(cx, i, nx, l2_next, bq, bdo, dqacc, k_lds[1], v_lds[1], k_lds[0], v_lds[0]);
+      i = nx;
+    }
   }
   // the row offset is formed again here from an opaque copy of the thread
   // index, so the compiler does not keep it live across the slot loop
