@@ -76,6 +76,63 @@ def test_training_step_replays_match_eager():
             assert torch.equal(val, eager[key]), (r, key)
 
 
+def test_decoding_steps_replay_through_the_one_call():
+    """Three decoding steps (one query chunk per head over a 3000-chunk context,
+    so that the retrieval is sliced and its merge runs inside the forward's
+    kernel) through gca_retrieve_forward, captured in one graph: every replay,
+    with eager work between replays, reproduces the eager steps' bits."""
+    cfg = synth.workload("infer1m_step", H=3, n_query=1, n_key=3000)
+    shape = shape_of(cfg)
+    gen = torch.Generator().manual_seed(11)
+    H, nk, steps = 3, 3000, 3
+
+    def mk(*shp, scale):
+        return (torch.randn(*shp, generator=gen) * scale).bfloat16().cuda()
+
+    lk = mk(1, 1, H, nk, 64, scale=1 / 8)
+    kk, v = mk(1, 1, H, nk, 64, 64, scale=0.125), mk(1, 1, H, nk, 64, 64, scale=0.125)
+    lqs = [mk(1, 1, H, 1, 64, scale=1 / 8) for _ in range(steps)]
+    qs = [mk(1, 1, H, 1, 64, 64, scale=0.125) for _ in range(steps)]
+    q_pos = torch.full((1,), nk + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(256, gca.gca_workspace_size(shape, gca.OP_RETRIEVE)), dtype=torch.uint8,
+                     device="cuda")
+    out = [dict(idx=torch.empty((1, 1, H, 1, 8), dtype=torch.int32, device="cuda"),
+                score=torch.empty((1, 1, H, 1, 8), device="cuda"),
+                w=torch.empty((1, 1, H, 1, 8), device="cuda"),
+                o=torch.empty_like(qs[0]), lse=torch.empty((1, 1, H, 1, 8, 64), device="cuda"))
+           for _ in range(steps)]
+
+    def body():
+        for s in range(steps):
+            b = out[s]
+            gca.gca_retrieve_forward(shape, lqs[s], lk, q_pos, qs[s], kk, v, b["idx"], b["score"],
+                                     b["w"], b["o"], b["lse"], ws=ws)
+
+    body()
+    torch.cuda.synchronize()
+    eager = [{key: val.clone() for key, val in b.items()} for b in out]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for b in out:
+            for val in b.values():
+                val.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            for key, val in out[s].items():
+                assert torch.equal(val, eager[s][key]), (r, s, key)
+
+
 def test_eager_backward_in_another_thread_during_a_capture():
     """A backward being captured on one thread and an eager backward on another
     thread's stream at the same time: each call enqueues on its own stream only,
