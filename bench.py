@@ -450,7 +450,8 @@ def bench_swa(steps):
 
     for _ in range(3):
         step()
-    ms, per = _timed(step, steps)
+    ms = _latency(step, steps)  # step time with the per-kernel events off
+    _, per = _timed(step, steps)
     pairs = B * H * swa_pairs(T, W)
     # algorithmic flops over the pairs inside the window: 2 products (QK, PV)
     # forward, 5 (QK, dO V^T, dQ, dK, dV) backward, 2*D flops each
@@ -501,7 +502,8 @@ def bench_train16k_fwd(steps, x=None):
 
     for _ in range(3):
         step()
-    ms, per = _timed(step, steps)
+    ms = _latency(step, steps)  # step time with the per-kernel events off
+    _, per = _timed(step, steps)
     pairs = int((idx >= 0).sum().item())
     wk = kernel_work(cfg, pairs)["forward"]
     fwd_s = per.get("forward", 0.0) * 1e-3
@@ -557,7 +559,8 @@ def bench_tile_sizes(steps):
 
         for _ in range(3):
             step()
-        ms, per = _timed(step, steps)
+        ms = _latency(step, steps)  # step time with the per-kernel events off
+        _, per = _timed(step, steps)
         out[f"S{S}_D{D}"] = {"chunk_size": S, "head_dim": D, "chunks_per_head": n,
                              "ms_per_step": round(ms, 4),
                              "tokens_per_s": round(B * n * S / (ms / 1e3), 1),
