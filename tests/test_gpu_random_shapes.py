@@ -12,7 +12,9 @@ README, "Model Architecture" (per-chunk attention and fusion); paperhub.cn,
 authors' reply "Cmt 1" (Eq. 1 scores); paperlayer.ai summary, appendix B
 (the backward's gradients).  Tolerances as everywhere: float32 1e-5 max-abs;
 bf16 2e-2 max-abs and 1e-2 mean-relative; indices bit-exact (inputs drawn with
-a 1e-3 gap at the k-th score).
+a 1e-3 gap at the k-th score).  A second set of bf16 cases has up to 59 more key
+chunks than query chunks and one case in ten with up to 699 chunks, and checks the
+one-call retrieval + forward against the two calls bit for bit.
 """
 
 import numpy as np
@@ -134,3 +136,59 @@ def test_random_retrieval_shape(seed):
     assert np.array_equal(idx.cpu().numpy()[sep], r_idx[sep])
     close("score", f64(score), r_score, True, mask=sep)
     close("w", f64(w), r_w, True, mask=sep)
+
+
+def _draw_grouped(seed):
+    """bf16 shapes the cases above leave out: more key chunks than query chunks
+    (up to 59 more, separate landmarks), one case in ten with 140 to 699 chunks (past
+    512 key chunks the reverse index takes a second pass)."""
+    rng = np.random.default_rng(3000 + seed)
+    name = ("train16k_fwd", "train16k_fwdbwd_g2")[rng.integers(2)]
+    big = rng.random() < 0.1
+    nq = int(rng.integers(140, 700) if big else rng.integers(1, 140))
+    nk = nq if name == "train16k_fwd" else nq + int(rng.integers(0, 60))
+    S, D = [(64, 64), (64, 32), (16, 64), (16, 32)][rng.integers(0, 4)]
+    G = 1 if name == "train16k_fwd" else int(rng.integers(1, 3))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    if big:
+        G, B, H = 1, 1, int(rng.integers(1, 3))
+    return name, dict(G=G, B=B, H=H, n_query=nq, n_key=nk, S=S, D=D,
+                      Dl=int((32, 64)[rng.integers(0, 2)]), k=int(rng.integers(1, 17)),
+                      softmax_one=int(rng.integers(0, 2)), seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_one_call_and_ragged_keys(seed):
+    """retrieve -> forward -> backward against the oracle, and the one-call
+    retrieval + forward (gca_retrieve_forward) equal to the two calls bit for bit."""
+    name, over = _draw_grouped(seed)
+    print(f"[random one-call] seed {seed}: {name} {over}", flush=True)
+    cfg = synth.workload(name, **over)
+    x = synth.training_inputs(name, accept=accept_for(cfg), **over)
+    shape = shape_of(cfg)
+    d = {key: dev(x[key]) for key in ("q", "k", "v", "lq", "lk", "dout", "q_pos")}
+    idx, score, w = run_retrieve(shape, d["lq"], d["lk"], d["q_pos"])
+    lq64, lk64 = f64(x["lq"]), f64(x["lk"])
+    r_idx, r_score, r_w = orc.retrieve(lq64, lk64, x["q_pos"].numpy(), cfg["k"],
+                                       cfg["score_scale"], cfg["softmax_one"])
+    assert np.array_equal(idx.cpu().numpy(), r_idx), "top-k indices differ"
+    close("score", f64(score), r_score, True)
+    close("w", f64(w), r_w, True)
+    o, lse = run_forward(shape, d["q"], d["k"], d["v"], idx, w)
+    q64, k64, v64, do64 = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"])
+    r_o, r_lse = orc.forward(q64, k64, v64, r_idx, r_w, cfg["attn_scale"])
+    close("o", f64(o), r_o, True)
+    compare_lse(lse, r_lse, True)
+    i2, s2, w2 = torch.full_like(idx, -7), torch.full_like(score, 7.0), torch.full_like(w, 7.0)
+    o2, l2 = torch.full_like(o, 7.0), torch.full_like(lse, 7.0)
+    gca.gca_retrieve_forward(shape, d["lq"], d["lk"], d["q_pos"], d["q"], d["k"], d["v"], i2, s2,
+                             w2, o2, l2)
+    torch.cuda.synchronize()
+    for nm, a, b in (("idx", idx, i2), ("score", score, s2), ("w", w, w2), ("o", o, o2),
+                     ("lse", lse, l2)):
+        assert torch.equal(torch.nan_to_num(a.float()), torch.nan_to_num(b.float())), nm
+    g = run_backward(shape, d["q"], d["k"], d["v"], idx, w, lse, d["dout"], d["lq"], d["lk"])
+    r = orc.backward(q64, k64, v64, r_idx, r_w, do64, lq64, lk64, cfg["attn_scale"],
+                     cfg["score_scale"])
+    for key in ("dq", "dk", "dv", "dw", "dscore", "dlq", "dlk"):
+        close(key, f64(g[key]), r[key], True)
