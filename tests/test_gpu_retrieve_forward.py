@@ -200,3 +200,46 @@ def test_retrieve_forward_other_paths(dtype_name):
         assert torch.equal(l1, lse2)
     r_o, _ = orc.forward(f64(q), f64(kk), f64(v), i2.cpu().numpy(), f64(w2), cfg["attn_scale"])
     close("o", f64(o2), r_o, bf)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_retrieve_forward_random_long_lists(seed):
+    """Random decoding and tile shapes (1..64 query chunks, 257..30000 candidates,
+    k 1..16, head_dim and landmark width 32 or 64, both weight variants, query
+    positions anywhere from no candidate to past the end): the one call equals
+    the two calls bit for bit, fused or not."""
+    rng = np.random.default_rng(4000 + seed)
+    H = int(rng.integers(1, 5))
+    nq = int(rng.choice([1, 2, 3, 4, 5, 9, 17, 33, 40, 64]))
+    nk, k = int(rng.integers(257, 30000)), int(rng.integers(1, 17))
+    D, dl, s1 = int(rng.choice([32, 64])), int(rng.choice([32, 64])), int(rng.integers(2))
+    print(f"[retrieve_forward random] seed {seed}: H={H} nq={nq} nk={nk} k={k} D={D} dl={dl} "
+          f"softmax_one={s1}", flush=True)
+    cfg = synth.workload("infer1m_step", H=H, n_query=nq, n_key=nk, k=k, D=D, Dl=dl,
+                         softmax_one=s1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+
+    def draw(*shape, scale):
+        return (torch.randn(shape, generator=gen, device="cuda") * scale).bfloat16()
+
+    lq, lk = draw(1, 1, H, nq, dl, scale=1 / 8), draw(1, 1, H, nk, dl, scale=1 / 8)
+    q, kk, v = (draw(1, 1, H, n, 64, D, scale=cfg["value_scale"]) for n in (nq, nk, nk))
+    q_pos = torch.from_numpy(rng.integers(0, nk + 2, size=nq).astype(np.int32)).cuda()
+    shape = shape_of(cfg)
+    slots = (1, 1, H, nq, k)
+
+    def outputs():
+        return (torch.full(slots, -7, dtype=torch.int32, device="cuda"),
+                torch.full(slots, 7.0, device="cuda"), torch.full(slots, 7.0, device="cuda"),
+                torch.full(tuple(q.shape), 7.0, dtype=torch.bfloat16, device="cuda"),
+                torch.full(slots + (64,), 7.0, device="cuda"))
+
+    a = outputs()
+    gca.gca_retrieve(shape, lq, lk, q_pos, a[0], a[1], a[2])
+    gca.gca_forward(shape, q, kk, v, a[0], a[2], a[3], a[4])
+    b = outputs()
+    gca.gca_retrieve_forward(shape, lq, lk, q_pos, q, kk, v, *b)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("idx", "score", "w", "o", "lse"), a, b):
+        assert torch.equal(torch.nan_to_num(x.float()), torch.nan_to_num(y.float())), name
