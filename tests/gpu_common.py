@@ -70,11 +70,15 @@ def run_backward(shape, q, k, v, idx, w, lse, dout, lq, lk):
     return dict(dq=dq, dk=dk, dv=dv, dw=dw, dscore=dscore, dlq=dlq, dlk=dlk)
 
 
-def close(name, got, ref, is_bf16_out, mask=None, terms=1):
+def close(name, got, ref, is_bf16_out, mask=None, terms=1, rel=0.0):
     """Asserts the tolerance for one tensor; returns (max_abs, mean_rel).
 
     terms > 1: `got` is a sum of that many results each held to the bound (a
-    group's layers), so the max-abs bound is terms times the per-result one."""
+    group's layers), so the max-abs bound is terms times the per-result one.
+    rel > 0 (bf16 outputs): each element may also differ by rel * |ref|, the
+    relative rounding of bf16 results and operands for elements well above 1,
+    where the fixed max-abs bound (sized for values of order 1) is less than
+    the output's own half ulp plus one operand rounding."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -89,7 +93,8 @@ def close(name, got, ref, is_bf16_out, mask=None, terms=1):
     mean_rel = float(err.mean() / denom) if denom > 0 else float(err.mean())
     if is_bf16_out:
         bound = terms * BF16_MAX_ABS
-        assert max_abs <= bound, f"{name}: max-abs {max_abs:.3g} > {bound}"
+        excess = float((err - rel * np.abs(ref)).max())
+        assert excess <= bound, f"{name}: max-abs {max_abs:.3g} (beyond {rel:g}|ref|: {excess:.3g}) > {bound}"
         assert mean_rel <= BF16_MEAN_REL, f"{name}: mean-rel {mean_rel:.3g} > {BF16_MEAN_REL}"
     else:
         bound = terms * F32_MAX_ABS

@@ -60,6 +60,28 @@ def test_swa_parity(B, H, T, W):
         close(name, got[name], ref, True)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_swa_random_shapes(seed):
+    """Random B (1..2), H (1..3), T (64..1536 in blocks of 64) and window (1..1600,
+    mostly not a multiple of 64): O, L and every gradient against the oracle.  With
+    unit-variance inputs a window of a few tokens gives gradients up to ~6, where
+    the output's own bf16 rounding (half an ulp, up to 2^-9 |x|) nearly fills the
+    2e-2 max-abs bound; each element may then also differ by 2^-8 |x| (the
+    output's rounding plus one rounding of a bf16 operand, P or dS)."""
+    rng = np.random.default_rng(5000 + seed)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    T, W = 64 * int(rng.integers(1, 25)), int(rng.integers(1, 1601))
+    print(f"[swa random] seed {seed}: B={B} H={H} T={T} window={W}", flush=True)
+    x = synth.swa_inputs(B, H, T, 64, seed=6000 + seed)
+    shape = gca.make_swa_shape(B, H, T, 64, W)
+    got = run_swa(shape, x)
+    q, k, v, do = (f64(x[n]) for n in ("q", "k", "v", "dout"))
+    o, lse = swa.swa_forward(q, k, v, W, shape.scale)
+    dq, dk, dv = swa.swa_backward(q, k, v, do, W, shape.scale)
+    for name, ref in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        close(name, got[name], ref, True, rel=2.0 ** -8)
+
+
 def test_swa_empty_sequence_is_a_no_op():
     shape = gca.make_swa_shape(2, 2, 0, 64, 512)
     z = torch.empty((2, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
